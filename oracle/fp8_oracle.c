@@ -1,0 +1,307 @@
+/*
+ * fp8_oracle.c -- plain, slow, obviously-correct CPU oracle for the FP8
+ * block-scaled quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the bench's
+ * cpu_baseline leg do.  It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * What it computes (source: the Jet-RL technical summary on gist.science,
+ * paper 2601.14243, section "Quantization scheme"; the numeric format and
+ * rounding are the project's stated definitions, listed per function):
+ *   - activations are quantized in 1x128 groups (one scale per row per 128
+ *     consecutive columns),
+ *   - weights are quantized in 128x128 blocks,
+ *   - the backward GEMMs (DGrad, WGrad) also run in FP8; WGrad groups both
+ *     operands 128-along-tokens (the page's "1x128 and 128x1" kernels),
+ *   - gradients between operators stay BF16; activations saved for backward
+ *     are FP8.
+ * Scale of a group = fp32(amax / 448), codes = E4M3(fp32(x / scale)) with
+ * round-to-nearest-even and saturation at +-448.  GEMMs are fp64 dot products
+ * of decoded codes times their scales.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
+ * (no FMA contraction, no flush-to-zero, IEEE single division).  OpenMP is
+ * used only across independent rows, so results do not depend on threads.
+ *
+ * Every function below is pinned by a CPU test against something other than
+ * itself (exhaustive brute force, closed forms, exact rationals or an
+ * independent library routine), except the FP8-source transpose-quant, whose
+ * requantization reading has no independent pin: parity unpinned for
+ * oracle_quant_transpose_fp8 beyond the invariants it shares with the rest.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define GROUP 128
+
+/* fp32 expressions must be evaluated in fp32 (no excess precision). */
+#if !defined(__FLT_EVAL_METHOD__) || __FLT_EVAL_METHOD__ != 0
+#error "the oracle needs FLT_EVAL_METHOD == 0 (x86-64 SSE or equivalent)"
+#endif
+
+/* ---------------------------------------------------------------- format */
+
+/*
+ * OCP E4M3FN decode: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits,
+ * no infinities, NaN only at 0x7F / 0xFF.  Exponent field 0 is subnormal:
+ * F * 2^-9; otherwise (8 + F) * 2^(E - 10).
+ */
+double oracle_e4m3_decode(uint8_t c)
+{
+    int s = (c >> 7) & 1;
+    int e = (c >> 3) & 0xF;
+    int f = c & 0x7;
+    double v;
+    if (e == 0xF && f == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)f, -9);
+    else
+        v = ldexp((double)(8 + f), e - 10);
+    return s ? -v : v;
+}
+
+/* Code of a non-negative magnitude that is exactly an E4M3 value <= 448. */
+static uint8_t e4m3_code_of_exact(double r)
+{
+    if (r < ldexp(1.0, -6)) {                 /* subnormal: r = F * 2^-9 */
+        return (uint8_t)(r * 512.0);
+    }
+    int e2;
+    double m = frexp(r, &e2);                 /* r = m * 2^e2, m in [0.5,1) */
+    int E = e2 - 1;                           /* r = (1 + F/8) * 2^E       */
+    int F = (int)((m * 2.0 - 1.0) * 8.0);
+    return (uint8_t)(((E + 7) << 3) | F);
+}
+
+/*
+ * fp32 -> E4M3 code.  Round |v| to the nearest E4M3 value; on a tie choose
+ * the value with the even code (equivalently, the even mantissa, which also
+ * holds across the subnormal/normal seam); magnitudes that round above 448
+ * saturate to 448 (0x7E).  The sign bit of v is kept, so -0 and negative
+ * values that round to zero give 0x80.  NaN/Inf inputs are outside the
+ * contract (the quantizer never produces them from finite inputs).
+ *
+ * Steps: the E4M3 quantum around |v| is 2^(E-3) with E = max(floor(log2|v|),
+ * -6); |v| / quantum is exact in fp64, nearbyint() rounds it to the nearest
+ * integer with ties to even; the product is the rounded magnitude.
+ */
+uint8_t oracle_e4m3_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;
+    if (E < -6)
+        E = -6;
+    double quantum = ldexp(1.0, E - 3);
+    double k = nearbyint(a / quantum);
+    double r = k * quantum;
+    if (r > 448.0)
+        return (uint8_t)(sign | 0x7E);
+    return (uint8_t)(sign | e4m3_code_of_exact(r));
+}
+
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/*
+ * fp64 -> bf16 with round-to-nearest-even (single rounding of the exact
+ * fp64 value).  Used to compare exactly-representable GEMM results.
+ */
+uint16_t oracle_f64_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;                           /* a in [2^E, 2^(E+1)) */
+    if (E < -126)
+        E = -126;                             /* bf16 subnormal quantum 2^-133 */
+    double quantum = ldexp(1.0, E - 7);
+    double r = nearbyint(a / quantum) * quantum;
+    if (r >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80);     /* overflow -> inf */
+    float f = (float)r;                       /* exact: r has <= 8 bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* ---------------------------------------------------------- quantization */
+
+/* One group: amax over n values (stride apart), scale, codes.  Steps of the
+ * definition: a = max|x| (exact in fp32); s = fp32(a / 448); q = E4M3(fp32(x
+ * / s)); an all-zero group gets s = 0 and signed-zero codes. */
+static float quant_group(const float* vals, int64_t n, uint8_t* codes)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float m = fabsf(vals[i]);
+        if (m > a)
+            a = m;
+    }
+    if (a == 0.0f) {
+        for (int64_t i = 0; i < n; ++i)
+            codes[i] = signbit(vals[i]) ? 0x80 : 0x00;
+        return 0.0f;
+    }
+    float s = a / 448.0f;                     /* IEEE fp32 division, RNE */
+    for (int64_t i = 0; i < n; ++i) {
+        float t = vals[i] / s;                /* IEEE fp32 division, RNE */
+        codes[i] = oracle_e4m3_encode(t);
+    }
+    return s;
+}
+
+/* Activation quant, 1x128 groups: x bf16 [M,K] -> q [M,K], s [M][K/128]. */
+void oracle_quant_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s)
+{
+    int64_t G = K / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float vals[GROUP];
+        uint8_t codes[GROUP];
+        for (int64_t g = 0; g < G; ++g) {
+            for (int i = 0; i < GROUP; ++i)
+                vals[i] = oracle_bf16_to_f32(x[m * K + g * GROUP + i]);
+            s[m * G + g] = quant_group(vals, GROUP, codes);
+            memcpy(q + m * K + g * GROUP, codes, GROUP);
+        }
+    }
+}
+
+/* Weight quant, 128x128 blocks aligned at (0,0): w bf16 [N,K] -> q [N,K],
+ * s [N/128][K/128] row-major. */
+void oracle_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s)
+{
+    int64_t BN = N / GROUP, BK = K / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < BN * BK; ++b) {
+        int64_t bi = b / BK, bj = b % BK;
+        float vals[GROUP * GROUP];
+        uint8_t codes[GROUP * GROUP];
+        for (int r = 0; r < GROUP; ++r)
+            for (int c = 0; c < GROUP; ++c)
+                vals[r * GROUP + c] =
+                    oracle_bf16_to_f32(w[(bi * GROUP + r) * K + bj * GROUP + c]);
+        s[bi * BK + bj] = quant_group(vals, GROUP * GROUP, codes);
+        for (int r = 0; r < GROUP; ++r)
+            memcpy(q + (bi * GROUP + r) * K + bj * GROUP, codes + r * GROUP, GROUP);
+    }
+}
+
+/* Transpose-quant from BF16, groups of 128 consecutive rows (tokens) per
+ * column: x bf16 [T,C] -> qT [C,T], sT [C][T/128]. */
+void oracle_quant_transpose_bf16(const uint16_t* x, int64_t T, int64_t C, uint8_t* qT, float* sT)
+{
+    int64_t G = T / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        float vals[GROUP];
+        uint8_t codes[GROUP];
+        for (int64_t g = 0; g < G; ++g) {
+            for (int i = 0; i < GROUP; ++i)
+                vals[i] = oracle_bf16_to_f32(x[(g * GROUP + i) * C + c]);
+            sT[c * G + g] = quant_group(vals, GROUP, codes);
+            memcpy(qT + c * T + g * GROUP, codes, GROUP);
+        }
+    }
+}
+
+/* Transpose-requant of a saved FP8 tensor (1x128 row-group scales along C):
+ * v = fp32(dec(q) * s_row) with a plain fp32 multiply, then the same
+ * 128-along-T quantization as above.  q [T,C], s_row [T][C/128] -> qT [C,T],
+ * sT [C][T/128].  Parity unpinned beyond shared invariants (see header). */
+void oracle_quant_transpose_fp8(const uint8_t* q, const float* s_row, int64_t T, int64_t C,
+                                uint8_t* qT, float* sT)
+{
+    int64_t G = T / GROUP, GC = C / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        float vals[GROUP];
+        uint8_t codes[GROUP];
+        for (int64_t g = 0; g < G; ++g) {
+            for (int i = 0; i < GROUP; ++i) {
+                int64_t t = g * GROUP + i;
+                float d = (float)oracle_e4m3_decode(q[t * C + c]);   /* exact */
+                vals[i] = d * s_row[t * GC + c / GROUP];             /* fp32 multiply */
+            }
+            sT[c * G + g] = quant_group(vals, GROUP, codes);
+            memcpy(qT + c * T + g * GROUP, codes, GROUP);
+        }
+    }
+}
+
+/* ------------------------------------------------------------ dequantize */
+
+/* out[r,c] = dec(q[r,c]) * s[r][c/128], in fp64 (exact: <= 28 significant
+ * bits). */
+void oracle_dequant_rowgroup(const uint8_t* q, const float* s, int64_t R, int64_t C, double* out)
+{
+    int64_t G = C / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c)
+            out[r * C + c] = oracle_e4m3_decode(q[r * C + c]) * (double)s[r * G + c / GROUP];
+}
+
+/* out[r,c] = dec(q[r,c]) * s[r/128][c/128], in fp64. */
+void oracle_dequant_block(const uint8_t* q, const float* s, int64_t R, int64_t C, double* out)
+{
+    int64_t G = C / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c)
+            out[r * C + c] =
+                oracle_e4m3_decode(q[r * C + c]) * (double)s[(r / GROUP) * G + c / GROUP];
+}
+
+/* ------------------------------------------------------------------ GEMM */
+
+/*
+ * C[m*N + n] = sum_{k ascending} A(m,k) * B(n,k) in fp64, where
+ * A(m,k) = A[m*sam + k*sak] and B(n,k) = B[n*sbn + k*sbk].  Strides let the
+ * same routine express the forward (X W^T), DGrad (dY W) and WGrad
+ * (dY^T X) contractions on dequantized operands.
+ */
+void oracle_gemm(int64_t M, int64_t N, int64_t K,
+                 const double* A, int64_t sam, int64_t sak,
+                 const double* B, int64_t sbn, int64_t sbk, double* C)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += A[m * sam + k * sak] * B[n * sbn + k * sbk];
+            C[m * N + n] = acc;
+        }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
