@@ -1,0 +1,240 @@
+"""Python binding of libfp8lin: FP8 block-scaled quantized linear layer on MI355X.
+
+Thin ctypes marshalling over the C ABI in ``include/fp8lin.h``; every step of
+the computation runs in the library's HIP kernels.  PyTorch only provides the
+device memory (output tensors) and the current HIP stream.  The functions keep
+the C names.  The library is loaded from this package directory and must have
+been built first (``python -m fp8_block_scaled_act_amd._build`` or
+``__graft_entry__.build()``); if it is missing, importing the functions raises.
+
+Tensor conventions: BF16 tensors are ``torch.bfloat16``; FP8 E4M3 codes are
+``torch.uint8``; scales are ``torch.float32``; everything is contiguous and on
+the current CUDA/HIP device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "lib", "Fp8LinError", "GROUP",
+    "fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose",
+    "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
+    "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
+    "SRC_BF16", "SRC_FP8_ROWQ",
+]
+
+GROUP = 128
+SRC_BF16 = 0
+SRC_FP8_ROWQ = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
+
+_SYMBOLS = {
+    # name: (argtypes, restype)
+    "fp8lin_version": ([], ctypes.c_int),
+    "fp8lin_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "fp8lin_last_hip_error": ([], ctypes.c_int),
+    "fp8_quant_act": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_void_p], ctypes.c_int),
+    "fp8_quant_weight": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                          ctypes.c_void_p], ctypes.c_int),
+    "fp8_quant_transpose": ([ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p], ctypes.c_int),
+    "fp8_gemm_fwd": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8_gemm_dgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8_gemm_wgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
+                           ctypes.c_int),
+    "fp8lin_decode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
+                           ctypes.c_int),
+}
+
+_lib = None
+
+
+class Fp8LinError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        text = lib().fp8lin_status_string(status).decode()
+        extra = ""
+        if status == 6:
+            extra = " (hipError_t %d)" % lib().fp8lin_last_hip_error()
+        super().__init__("%s: %s%s" % (where, text, extra))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfp8lin (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libfp8lin.so is not built at %s; run __graft_entry__.build() or "
+                              "python -m fp8_block_scaled_act_amd._build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SYMBOLS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise Fp8LinError(status, where)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() and not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+
+
+def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# --------------------------------------------------------------- quantization
+
+def fp8_quant_act(x: torch.Tensor, out=None, stream=None):
+    """1x128 row-group quantization: x bf16 [M,K] -> (codes u8 [M,K], scales f32 [M,K/128])."""
+    M, K = x.shape
+    _expect(x, "x", torch.bfloat16, (M, K))
+    q, s = out if out is not None else (_empty((M, K), torch.uint8, x), _empty((M, K // GROUP), torch.float32, x))
+    _expect(q, "xq", torch.uint8, (M, K))
+    _expect(s, "sx", torch.float32, (M, K // GROUP))
+    _check(lib().fp8_quant_act(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(stream)), "fp8_quant_act")
+    return q, s
+
+
+def fp8_quant_weight(w: torch.Tensor, out=None, stream=None):
+    """128x128 block quantization: w bf16 [N,K] -> (codes u8 [N,K], scales f32 [N/128,K/128])."""
+    N, K = w.shape
+    _expect(w, "w", torch.bfloat16, (N, K))
+    q, s = out if out is not None else (_empty((N, K), torch.uint8, w),
+                                        _empty((N // GROUP, K // GROUP), torch.float32, w))
+    _expect(q, "wq", torch.uint8, (N, K))
+    _expect(s, "sw", torch.float32, (N // GROUP, K // GROUP))
+    _check(lib().fp8_quant_weight(_ptr(w), N, K, _ptr(q), _ptr(s), _stream(stream)), "fp8_quant_weight")
+    return q, s
+
+
+def fp8_quant_transpose(src: torch.Tensor, src_scales: torch.Tensor | None = None, dual: bool = False,
+                        out=None, stream=None):
+    """128-along-T quantization written transposed (WGrad operands).
+
+    src bf16 [T,C] (src_scales None), or saved FP8 codes u8 [T,C] with 1x128
+    scales f32 [T,C/128].  Returns (codesT u8 [C,T], scalesT f32 [C,T/128]) and,
+    with dual=True (BF16 only), also (codes u8 [T,C], scales f32 [T,C/128]) of
+    the 1x128 row quantization from the same read."""
+    T, C = src.shape
+    if src_scales is None:
+        kind = SRC_BF16
+        _expect(src, "src", torch.bfloat16, (T, C))
+    else:
+        kind = SRC_FP8_ROWQ
+        _expect(src, "src", torch.uint8, (T, C))
+        _expect(src_scales, "src_scales", torch.float32, (T, C // GROUP))
+    if out is None:
+        qT, sT = _empty((C, T), torch.uint8, src), _empty((C, T // GROUP), torch.float32, src)
+        qr = sr = None
+        if dual:
+            qr, sr = _empty((T, C), torch.uint8, src), _empty((T, C // GROUP), torch.float32, src)
+    else:
+        qT, sT, qr, sr = out
+    _expect(qT, "dstT", torch.uint8, (C, T))
+    _expect(sT, "sT", torch.float32, (C, T // GROUP))
+    if qr is not None:
+        _expect(qr, "dst_rowq", torch.uint8, (T, C))
+        _expect(sr, "s_rowq", torch.float32, (T, C // GROUP))
+    _check(lib().fp8_quant_transpose(kind, _ptr(src), _ptr(src_scales), T, C, _ptr(qT), _ptr(sT), _ptr(qr),
+                                     _ptr(sr), _stream(stream)), "fp8_quant_transpose")
+    return (qT, sT, qr, sr) if dual else (qT, sT)
+
+
+# ---------------------------------------------------------------------- GEMMs
+
+def fp8_gemm_fwd(xq, sx, wq, sw, out=None, stream=None):
+    """Y[M,N] bf16 = X W^T from 1x128-quantized X [M,K] and 128x128-quantized W [N,K]."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    _expect(xq, "xq", torch.uint8, (M, K))
+    _expect(sx, "sx", torch.float32, (M, K // GROUP))
+    _expect(wq, "wq", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    y = out if out is not None else _empty((M, N), torch.bfloat16, xq)
+    _expect(y, "y", torch.bfloat16, (M, N))
+    _check(lib().fp8_gemm_fwd(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
+           "fp8_gemm_fwd")
+    return y
+
+
+def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):
+    """dX[T,K] bf16 = dY W from 1x128-quantized dY [T,N] and 128x128-quantized W [N,K]."""
+    T, N = dyq.shape
+    K = wq.shape[1]
+    _expect(dyq, "dyq", torch.uint8, (T, N))
+    _expect(sdy, "sdy", torch.float32, (T, N // GROUP))
+    _expect(wq, "wq", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    dx = out if out is not None else _empty((T, K), torch.bfloat16, dyq)
+    _expect(dx, "dx", torch.bfloat16, (T, K))
+    _check(lib().fp8_gemm_dgrad(_ptr(dyq), _ptr(sdy), _ptr(wq), _ptr(sw), T, N, K, _ptr(dx), _stream(stream)),
+           "fp8_gemm_dgrad")
+    return dx
+
+
+def fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT, out=None, stream=None):
+    """dW[N,K] bf16 = dY^T X from operands grouped 128-along-T: dY^T [N,T], X^T [K,T]."""
+    N, T = dyTq.shape
+    K = xTq.shape[0]
+    _expect(dyTq, "dyTq", torch.uint8, (N, T))
+    _expect(sdyT, "sdyT", torch.float32, (N, T // GROUP))
+    _expect(xTq, "xTq", torch.uint8, (K, T))
+    _expect(sxT, "sxT", torch.float32, (K, T // GROUP))
+    dw = out if out is not None else _empty((N, K), torch.bfloat16, dyTq)
+    _expect(dw, "dw", torch.bfloat16, (N, K))
+    _check(lib().fp8_gemm_wgrad(_ptr(dyTq), _ptr(sdyT), _ptr(xTq), _ptr(sxT), N, K, T, _ptr(dw),
+                                _stream(stream)), "fp8_gemm_wgrad")
+    return dw
+
+
+# ---------------------------------------------------------------- diagnostics
+
+def fp8lin_encode_e4m3(x: torch.Tensor, method: int = 0, out=None, stream=None):
+    """Device fp32 -> E4M3 encoder on a flat float32 tensor (method 0 = kernels')."""
+    _expect(x, "in", torch.float32, tuple(x.shape))
+    q = out if out is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().fp8lin_encode_e4m3(_ptr(x), x.numel(), _ptr(q), method, _stream(stream)), "fp8lin_encode_e4m3")
+    return q
+
+
+def fp8lin_decode_e4m3(q: torch.Tensor, method: int = 0, out=None, stream=None):
+    """Device E4M3 -> fp32 decoder on a flat uint8 tensor (method 0 = kernels')."""
+    _expect(q, "in", torch.uint8, tuple(q.shape))
+    x = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(lib().fp8lin_decode_e4m3(_ptr(q), q.numel(), _ptr(x), method, _stream(stream)), "fp8lin_decode_e4m3")
+    return x

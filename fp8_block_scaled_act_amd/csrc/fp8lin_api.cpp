@@ -1,0 +1,389 @@
+// fp8lin_api.cpp -- the C ABI of libfp8lin (declared in include/fp8lin.h).
+//
+// Each entry point validates its arguments on the host (pure checks, no HIP
+// call), then checks once per device that it is a gfx950, then enqueues the
+// kernels on the caller's stream and returns.  Nothing is allocated.
+#include "fp8lin.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "fp8lin_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kGroup = FP8LIN_GROUP;
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxBlocks = 0x7FFFFFFF;
+
+// ---------------------------------------------------------------- checks
+
+struct Buf {
+    const void* p;
+    int64_t bytes;
+};
+
+// a * b * c with overflow detection (all operands >= 0).
+bool mul_ok(int64_t a, int64_t b, int64_t* out)
+{
+    if (a == 0 || b == 0) {
+        *out = 0;
+        return true;
+    }
+    if (a > INT64_MAX / b)
+        return false;
+    *out = a * b;
+    return true;
+}
+
+bool bytes_of(int64_t rows, int64_t cols, int64_t elem, int64_t* out)
+{
+    int64_t n;
+    return mul_ok(rows, cols, &n) && mul_ok(n, elem, out);
+}
+
+bool overlap(const Buf& x, const Buf& y)
+{
+    if (x.bytes <= 0 || y.bytes <= 0)
+        return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), a1 = a0 + (uintptr_t)x.bytes;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(y.p), b1 = b0 + (uintptr_t)y.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+// NULL / alignment / aliasing of the buffers a call touches.  Buffers with 0
+// bytes are not touched and may be anything.
+fp8lin_status check_buffers(const Buf* in, int nin, const Buf* out, int nout)
+{
+    for (int i = 0; i < nin + nout; ++i) {
+        const Buf& b = i < nin ? in[i] : out[i - nin];
+        if (b.bytes > 0 && b.p == nullptr)
+            return FP8LIN_ERR_NULL;
+    }
+    for (int i = 0; i < nin + nout; ++i) {
+        const Buf& b = i < nin ? in[i] : out[i - nin];
+        if (b.bytes > 0 && (reinterpret_cast<uintptr_t>(b.p) & 15u) != 0)
+            return FP8LIN_ERR_ALIGN;
+    }
+    for (int o = 0; o < nout; ++o) {
+        for (int i = 0; i < nin; ++i)
+            if (overlap(out[o], in[i]))
+                return FP8LIN_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < nout; ++o2)
+            if (overlap(out[o], out[o2]))
+                return FP8LIN_ERR_ALIAS;
+    }
+    return FP8LIN_OK;
+}
+
+// ----------------------------------------------------------- device check
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+fp8lin_status check_device()
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return FP8LIN_ERR_DEVICE;
+    }
+    if (dev < kMaxDevices) {
+        const int st = g_arch_state[dev].load(std::memory_order_acquire);
+        if (st == 1)
+            return FP8LIN_OK;
+        if (st == 2)
+            return FP8LIN_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return FP8LIN_ERR_DEVICE;
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices)
+        g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+    return ok ? FP8LIN_OK : FP8LIN_ERR_DEVICE;
+}
+
+// Device check, then clear any stale error so the post-launch check sees
+// only this call's launches.
+fp8lin_status begin_launch()
+{
+    const fp8lin_status s = check_device();
+    if (s != FP8LIN_OK)
+        return s;
+    (void)hipGetLastError();
+    return FP8LIN_OK;
+}
+
+fp8lin_status end_launch()
+{
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return FP8LIN_ERR_HIP;
+    }
+    return FP8LIN_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int fp8lin_version(void) { return FP8LIN_VERSION; }
+
+const char* fp8lin_status_string(int status)
+{
+    switch (status) {
+    case FP8LIN_OK: return "FP8LIN_OK: success";
+    case FP8LIN_ERR_NULL: return "FP8LIN_ERR_NULL: a required pointer is NULL";
+    case FP8LIN_ERR_SHAPE: return "FP8LIN_ERR_SHAPE: invalid size (negative, 128-group dimension not a multiple of 128, or too large)";
+    case FP8LIN_ERR_ALIGN: return "FP8LIN_ERR_ALIGN: a base pointer is not 16-byte aligned";
+    case FP8LIN_ERR_ALIAS: return "FP8LIN_ERR_ALIAS: an output overlaps an input or another output";
+    case FP8LIN_ERR_DEVICE: return "FP8LIN_ERR_DEVICE: no HIP device, or the current device is not gfx950";
+    case FP8LIN_ERR_HIP: return "FP8LIN_ERR_HIP: a HIP call or kernel launch failed";
+    case FP8LIN_ERR_ARG: return "FP8LIN_ERR_ARG: invalid argument combination";
+    default: return "FP8LIN: unknown status";
+    }
+}
+
+int fp8lin_last_hip_error(void) { return g_last_hip_error; }
+
+fp8lin_status fp8_quant_act(const void* x, int64_t M, int64_t K, uint8_t* xq, float* sx, void* stream)
+{
+    if (M < 0 || K < 0 || K % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bx, bq, bs;
+    if (!bytes_of(M, K, 2, &bx) || !bytes_of(M, K, 1, &bq) || !bytes_of(M, K / kGroup, 4, &bs))
+        return FP8LIN_ERR_SHAPE;
+    const Buf in[] = {{x, bx}};
+    const Buf out[] = {{xq, bq}, {sx, bs}};
+    fp8lin_status s = check_buffers(in, 1, out, 2);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bq == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_quant_rowgroup(x, M * (K / kGroup), xq, sx, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8_quant_weight(const void* w, int64_t N, int64_t K, uint8_t* wq, float* sw, void* stream)
+{
+    if (N < 0 || K < 0 || N % kGroup != 0 || K % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    if (N / kGroup > kMaxGridY)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bw, bq, bs;
+    if (!bytes_of(N, K, 2, &bw) || !bytes_of(N, K, 1, &bq) || !bytes_of(N / kGroup, K / kGroup, 4, &bs))
+        return FP8LIN_ERR_SHAPE;
+    const Buf in[] = {{w, bw}};
+    const Buf out[] = {{wq, bq}, {sw, bs}};
+    fp8lin_status s = check_buffers(in, 1, out, 2);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bq == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_quant_block(w, N, K, wq, sw, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8_quant_transpose(int kind, const void* src, const float* src_scales, int64_t T, int64_t C,
+                                  uint8_t* dstT, float* sT, uint8_t* dst_rowq, float* s_rowq, void* stream)
+{
+    if (kind != FP8LIN_SRC_BF16 && kind != FP8LIN_SRC_FP8_ROWQ)
+        return FP8LIN_ERR_ARG;
+    const bool dual = dst_rowq != nullptr || s_rowq != nullptr;
+    if (dual && (dst_rowq == nullptr || s_rowq == nullptr))
+        return FP8LIN_ERR_NULL;
+    if (kind == FP8LIN_SRC_FP8_ROWQ && dual)
+        return FP8LIN_ERR_ARG;
+    if (kind == FP8LIN_SRC_BF16 && src_scales != nullptr)
+        return FP8LIN_ERR_ARG;
+    if (T < 0 || C < 0 || T % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    if ((kind == FP8LIN_SRC_FP8_ROWQ || dual) && C % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    if (T / kGroup > kMaxGridY || (C + kGroup - 1) / kGroup > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    const int64_t elem = kind == FP8LIN_SRC_BF16 ? 2 : 1;
+    int64_t bsrc, bss = 0, bq, bs, bqr = 0, bsr = 0;
+    if (!bytes_of(T, C, elem, &bsrc) || !bytes_of(T, C, 1, &bq) || !bytes_of(C, T / kGroup, 4, &bs))
+        return FP8LIN_ERR_SHAPE;
+    if (kind == FP8LIN_SRC_FP8_ROWQ) {
+        if (src_scales == nullptr)
+            return T * C == 0 ? FP8LIN_OK : FP8LIN_ERR_ARG;
+        if (!bytes_of(T, C / kGroup, 4, &bss))
+            return FP8LIN_ERR_SHAPE;
+    }
+    if (dual) {
+        bqr = bq;
+        if (!bytes_of(T, C / kGroup, 4, &bsr))
+            return FP8LIN_ERR_SHAPE;
+    }
+    const Buf in[] = {{src, bsrc}, {src_scales, bss}};
+    const Buf out[] = {{dstT, bq}, {sT, bs}, {dst_rowq, bqr}, {s_rowq, bsr}};
+    fp8lin_status s = check_buffers(in, 2, out, 4);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bq == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    if (kind == FP8LIN_SRC_BF16)
+        fp8lin::launch_quant_transpose_bf16(src, T, C, dstT, sT, dual ? dst_rowq : nullptr,
+                                            dual ? s_rowq : nullptr, as_stream(stream));
+    else
+        fp8lin::launch_quant_transpose_fp8(static_cast<const uint8_t*>(src), src_scales, T, C, dstT, sT,
+                                           as_stream(stream));
+    return end_launch();
+}
+
+// Shared checks of the three GEMMs.  C = sum over Kc of A [M,Kc] x B.
+static fp8lin_status gemm_common(const Buf* in, int64_t M, int64_t N, int64_t Kc, void* c, int64_t* bc)
+{
+    int64_t tm = (M + 127) / 128, tn = (N + 127) / 128, nb;
+    if (!mul_ok(tm, tn, &nb) || nb > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    if (!bytes_of(M, N, 2, bc))
+        return FP8LIN_ERR_SHAPE;
+    (void)Kc;
+    const Buf out[] = {{c, *bc}};
+    return check_buffers(in, 4, out, 1);
+}
+
+fp8lin_status fp8_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                           int64_t N, int64_t K, void* y, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || N % kGroup != 0 || K % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bx, bsx, bw, bsw, by;
+    if (!bytes_of(M, K, 1, &bx) || !bytes_of(M, K / kGroup, 4, &bsx) || !bytes_of(N, K, 1, &bw) ||
+        !bytes_of(N / kGroup, K / kGroup, 4, &bsw))
+        return FP8LIN_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        bx = bsx = bw = bsw = 0;
+    const Buf in[] = {{xq, bx}, {sx, bsx}, {wq, bw}, {sw, bsw}};
+    fp8lin_status s = gemm_common(in, M, N, K, y, &by);
+    if (s != FP8LIN_OK)
+        return s;
+    if (by == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    if (K == 0)
+        fp8lin::launch_fill_zero_bf16(y, M * N, as_stream(stream));
+    else
+        fp8lin::launch_gemm_fwd(xq, sx, wq, sw, M, N, K, y, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t T,
+                             int64_t N, int64_t K, void* dx, void* stream)
+{
+    if (T < 0 || N < 0 || K < 0 || N % kGroup != 0 || K % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bdy, bsdy, bw, bsw, bdx;
+    if (!bytes_of(T, N, 1, &bdy) || !bytes_of(T, N / kGroup, 4, &bsdy) || !bytes_of(N, K, 1, &bw) ||
+        !bytes_of(N / kGroup, K / kGroup, 4, &bsw))
+        return FP8LIN_ERR_SHAPE;
+    if (T == 0 || K == 0)
+        bdy = bsdy = bw = bsw = 0;
+    const Buf in[] = {{dyq, bdy}, {sdy, bsdy}, {wq, bw}, {sw, bsw}};
+    fp8lin_status s = gemm_common(in, T, K, N, dx, &bdx);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bdx == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    if (N == 0)
+        fp8lin::launch_fill_zero_bf16(dx, T * K, as_stream(stream));
+    else
+        fp8lin::launch_gemm_dgrad(dyq, sdy, wq, sw, T, N, K, dx, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,
+                             int64_t N, int64_t K, int64_t T, void* dw, void* stream)
+{
+    if (N < 0 || K < 0 || T < 0 || T % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bdy, bsdy, bx, bsx, bdw;
+    if (!bytes_of(N, T, 1, &bdy) || !bytes_of(N, T / kGroup, 4, &bsdy) || !bytes_of(K, T, 1, &bx) ||
+        !bytes_of(K, T / kGroup, 4, &bsx))
+        return FP8LIN_ERR_SHAPE;
+    if (N == 0 || K == 0)
+        bdy = bsdy = bx = bsx = 0;
+    const Buf in[] = {{dyTq, bdy}, {sdyT, bsdy}, {xTq, bx}, {sxT, bsx}};
+    fp8lin_status s = gemm_common(in, N, K, T, dw, &bdw);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bdw == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    if (T == 0)
+        fp8lin::launch_fill_zero_bf16(dw, N * K, as_stream(stream));
+    else
+        fp8lin::launch_gemm_wgrad(dyTq, sdyT, xTq, sxT, N, K, T, dw, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8lin_encode_e4m3(const float* in, int64_t n, uint8_t* out, int method, void* stream)
+{
+    if (n < 0)
+        return FP8LIN_ERR_SHAPE;
+    if (method < 0 || method > 2)
+        return FP8LIN_ERR_ARG;
+    int64_t bi;
+    if (!mul_ok(n, 4, &bi) || n / 1024 + 1 > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    const Buf ib[] = {{in, bi}};
+    const Buf ob[] = {{out, n}};
+    fp8lin_status s = check_buffers(ib, 1, ob, 1);
+    if (s != FP8LIN_OK)
+        return s;
+    if (n == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_encode_probe(in, n, out, method, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int method, void* stream)
+{
+    if (n < 0)
+        return FP8LIN_ERR_SHAPE;
+    if (method < 0 || method > 2)
+        return FP8LIN_ERR_ARG;
+    int64_t bo;
+    if (!mul_ok(n, 4, &bo) || n / 1024 + 1 > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    const Buf ib[] = {{in, n}};
+    const Buf ob[] = {{out, bo}};
+    fp8lin_status s = check_buffers(ib, 1, ob, 1);
+    if (s != FP8LIN_OK)
+        return s;
+    if (n == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_decode_probe(in, n, out, method, as_stream(stream));
+    return end_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// fp8lin_launch.hpp -- internal launchers behind the C ABI (not exported).
+// Every launcher only enqueues on `st`; arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+void launch_quant_rowgroup(const void* x, int64_t ngroups, uint8_t* q, float* s, hipStream_t st);
+void launch_quant_block(const void* w, int64_t N, int64_t K, uint8_t* q, float* s, hipStream_t st);
+void launch_quant_transpose_bf16(const void* x, int64_t T, int64_t C, uint8_t* qT, float* sT,
+                                 uint8_t* qrow, float* srow, hipStream_t st);
+void launch_quant_transpose_fp8(const uint8_t* src, const float* srow, int64_t T, int64_t C,
+                                uint8_t* qT, float* sT, hipStream_t st);
+void launch_encode_probe(const float* in, int64_t n, uint8_t* out, int method, hipStream_t st);
+void launch_decode_probe(const uint8_t* in, int64_t n, float* out, int method, hipStream_t st);
+
+void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st);
+void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                     int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
+void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
+                       int64_t T, int64_t N, int64_t K, void* dx, hipStream_t st);
+void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,
+                       int64_t N, int64_t K, int64_t T, void* dw, hipStream_t st);
+
+}  // namespace fp8lin

@@ -1,0 +1,420 @@
+// gemm_kernels.hip -- block-scaled FP8 GEMMs for gfx950.
+//
+// Jet-RL technical summary (gist.science 2601.14243), "Quantization scheme":
+// the forward GEMM, the DGrad GEMM and the WGrad GEMM all run on FP8 codes,
+// 1x128-grouped activations/gradients and 128x128-blocked weights (WGrad on
+// operands grouped 128-along-tokens).  Every 128-wide contraction group g has
+// one scale per row of the left operand and one per column (or per 128-column
+// block) of the right operand:
+//     C[m,n] = sum_g sa[m,g] * sb[n,g] * P_g[m,n],
+//     P_g[m,n] = sum_{k in g} dec(A[m,k]) * dec(B[n,k]),
+// with P_g promoted into fp32 accumulators once per group.
+//
+// Matrix-core choice.  gfx950's FP8 MFMA sums its products in a fixed-point
+// window: products are aligned to the largest one of a chunk and truncated
+// toward zero 13 bits below it (measured: 448 + 0.0586 in adjacent slots gives
+// 448.03125; errors reach 2^-11.6 of the largest product on random codes).
+// With the outlier channels of real activations that error exceeds the
+// layer's accuracy bound.  Every E4M3 value is exactly an fp16 value, so the
+// codes are converted exactly to fp16 while they are staged into LDS
+// (v_cvt_pk_f32_fp8 + v_cvt_pkrtz_f16_f32) and multiplied on the fp16 matrix
+// core (v_mfma_f32_16x16x32_f16, measured error <= 2^-20 of the largest
+// product).  HBM traffic stays one byte per operand element.
+//
+// One workgroup: 256 threads = 4 waves on a WM x WN grid, tile BM x BN of C,
+// contraction stepped one group (128) at a time:
+//   - FP8 operand tiles are read from global (16-byte loads), converted and
+//     written to LDS as fp16, double-buffered: group g+1 is in flight while
+//     group g is multiplied;
+//   - an LDS row is one group of one row (column) of an operand: 16 chunks of
+//     8 fp16.  Chunk p holds k in [16 (p mod 8) + 8 (p div 8), +8): a fixed
+//     permutation of the group applied to both operands, which leaves the
+//     contraction unchanged and lets 8 threads write a row without bank
+//     conflicts.  Chunks are XOR-swizzled with swz(row) so fragment reads of 16
+//     rows hit distinct banks;
+//   - one group = 4 chained 16x16x32 MFMAs (fp32 C operand, exact fp32 adds);
+//     lane l supplies row (l % 16) and chunk 4 s + l / 16 for step s;
+//     output lane l, register v: row 4 (l / 16) + v, column l % 16.
+//   - promotion: acc += P_g * (sa * sb) with one fp32 FMA per element.
+//
+// DGrad contracts W [N,K] over its rows: the B tile (128 rows of W x BN
+// columns) is read along W's rows (coalesced), transposed 4x4 bytes at a
+// time in registers with v_perm and stored column-major, so the MFMA side is
+// the same as for the NT products.  128x128 weight blocks make the transpose
+// exact (the block-scale grid transposes).
+#include "fp8lin_device.hpp"
+#include "fp8lin_launch.hpp"
+
+namespace fp8lin {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+enum class Mode { Fwd = 0, Dgrad = 1, Wgrad = 2 };
+
+struct GemmArgs {
+    const uint8_t* a;   // [M][Kc] codes
+    const float* sa;    // [M][G]
+    const uint8_t* b;   // Fwd/Wgrad: [N][Kc]; Dgrad: [Kc][N]
+    const float* sb;    // Fwd: [N/128][G]; Dgrad: [G][N/128]; Wgrad: [N][G]
+    uint16_t* c;        // bf16 [M][N]
+    int64_t M, N, Kc;
+    int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 2)) & 7; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// 4 E4M3 codes -> 4 fp16 (exact: every E4M3 value is an fp16 value).
+__device__ __forceinline__ u32x2 fp8x4_to_f16x4(uint32_t w)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+    const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    const h2 a = __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y);
+    const h2 b = __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y);
+    return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+// 16 codes (one 16-byte FP8 chunk) -> 32 bytes of fp16 as two 16-byte halves.
+__device__ __forceinline__ void fp8x16_to_f16(u32x4 v, u32x4& lo, u32x4& hi)
+{
+    const u32x2 a = fp8x4_to_f16x4(v.x), b = fp8x4_to_f16x4(v.y);
+    const u32x2 c = fp8x4_to_f16x4(v.z), d = fp8x4_to_f16x4(v.w);
+    lo = u32x4{a.x, a.y, b.x, b.y};
+    hi = u32x4{c.x, c.y, d.x, d.y};
+}
+
+// 4x4 byte transpose: rows r0..r3 (4 bytes each) -> columns c0..c3.
+__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                             uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3)
+{
+    const uint32_t lo01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+    c0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    c1 = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    c2 = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    c3 = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+// Byte offset in an LDS row (256 bytes = 16 fp16 chunks) of logical chunk p.
+__device__ __forceinline__ int lds_chunk(int row, int p) { return row * 256 + ((p ^ swz(row)) << 4); }
+
+// XCD-aware block order: hardware dispatches workgroup i to XCD i % 8.  The
+// remap makes consecutive remapped ids live on one XCD (bijective for any
+// count), then a grouped raster (GROUP_M row-tiles per band) keeps tiles that
+// share A rows and B columns close in time on the same L2.
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm,
+                                            int& tn)
+{
+    constexpr int kXcd = 8;
+    constexpr int kGroupM = 8;
+    const int q = nblocks / kXcd, r = nblocks % kXcd;
+    const int xcd = bid % kXcd, idx = bid / kXcd;
+    const int id = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    const int in_group = kGroupM * tiles_n;
+    const int gid = id / in_group;
+    const int first_m = gid * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    const int local = id % in_group;
+    tm = first_m + local % gsize;
+    tn = local / gsize;
+}
+
+template <int BM, int BN, int WM, int WN, Mode MODE>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p)
+{
+    static_assert(WM * WN == 4, "4 waves");
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    static_assert(TM >= 1 && TN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    constexpr int A_CHUNKS = BM * 8 / 256;          // 16-byte FP8 chunks per thread
+    constexpr int B_CHUNKS = BN * 8 / 256;
+    static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
+    constexpr int DG_ROWS = BN / 8;                 // Dgrad: W rows per thread (8 or 16)
+    static_assert(MODE != Mode::Dgrad || DG_ROWS == 8 || DG_ROWS == 16, "Dgrad tile");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * 256];
+    __shared__ __attribute__((aligned(16))) float lds_sa[2][BM];
+    __shared__ __attribute__((aligned(16))) float lds_sb[2][MODE == Mode::Wgrad ? BN : 4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int lr = lane & 15, kg = lane >> 4;
+
+    int tmi, tni;
+    tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tmi, tni);
+    const int64_t m0 = (int64_t)tmi * BM;
+    const int64_t n0 = (int64_t)tni * BN;
+    const int64_t G = p.Kc / kGroup;
+
+    // ------------------------------------------------ stage registers
+    u32x4 ra[A_CHUNKS];
+    u32x4 rb[MODE == Mode::Dgrad ? 1 : B_CHUNKS];
+    uint32_t rbd[MODE == Mode::Dgrad ? DG_ROWS : 1];
+    float rsa = 0.f, rsb = 0.f;
+
+    auto load_global = [&](int64_t g) {
+        const int64_t k0 = g * kGroup;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx >> 3, c = idx & 7;
+            int64_t row = m0 + r;
+            row = row < p.M ? row : p.M - 1;
+            ra[i] = *reinterpret_cast<const u32x4*>(p.a + row * p.Kc + k0 + c * 16);
+        }
+        if constexpr (MODE == Mode::Dgrad) {
+            constexpr int KQ = BN / 4;              // 4-column groups across the tile
+            const int kq = tid % KQ, rbk = tid / KQ;
+            const uint8_t* base = p.b + (k0 + rbk * DG_ROWS) * p.N + n0 + kq * 4;
+#pragma unroll
+            for (int j = 0; j < DG_ROWS; ++j)
+                rbd[j] = *reinterpret_cast<const uint32_t*>(base + j * p.N);
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CHUNKS; ++i) {
+                const int idx = tid + 256 * i;
+                const int r = idx >> 3, c = idx & 7;
+                int64_t row = n0 + r;
+                row = row < p.N ? row : p.N - 1;
+                rb[i] = *reinterpret_cast<const u32x4*>(p.b + row * p.Kc + k0 + c * 16);
+            }
+        }
+        if (tid < BM) {
+            int64_t row = m0 + tid;
+            row = row < p.M ? row : p.M - 1;
+            rsa = p.sa[row * G + g];
+        }
+        if constexpr (MODE == Mode::Wgrad) {
+            if (tid >= 128 && tid < 128 + BN) {
+                int64_t col = n0 + (tid - 128);
+                col = col < p.N ? col : p.N - 1;
+                rsb = p.sb[col * G + g];
+            }
+        }
+    };
+
+    auto store_lds = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx >> 3, c = idx & 7;
+            u32x4 lo, hi;
+            fp8x16_to_f16(ra[i], lo, hi);
+            *reinterpret_cast<u32x4*>(&lds_a[buf][lds_chunk(r, c)]) = lo;
+            *reinterpret_cast<u32x4*>(&lds_a[buf][lds_chunk(r, c + 8)]) = hi;
+        }
+        if constexpr (MODE == Mode::Dgrad) {
+            constexpr int KQ = BN / 4;
+            const int kq = tid % KQ, rbk = tid / KQ;
+            uint32_t cols[4][DG_ROWS / 4];
+#pragma unroll
+            for (int j = 0; j < DG_ROWS / 4; ++j)
+                transpose4x4(rbd[4 * j], rbd[4 * j + 1], rbd[4 * j + 2], rbd[4 * j + 3], cols[0][j],
+                             cols[1][j], cols[2][j], cols[3][j]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = kq * 4 + q;
+                if constexpr (DG_ROWS == 16) {
+                    // rows [16 rbk, 16 rbk + 16) of the group = FP8 chunk rbk
+                    u32x4 lo, hi;
+                    fp8x16_to_f16(u32x4{cols[q][0], cols[q][1], cols[q][2], cols[q][3]}, lo, hi);
+                    *reinterpret_cast<u32x4*>(&lds_b[buf][lds_chunk(col, rbk)]) = lo;
+                    *reinterpret_cast<u32x4*>(&lds_b[buf][lds_chunk(col, rbk + 8)]) = hi;
+                } else {
+                    // rows [8 rbk, 8 rbk + 8) = half (rbk & 1) of FP8 chunk rbk / 2
+                    const u32x2 a = fp8x4_to_f16x4(cols[q][0]), b = fp8x4_to_f16x4(cols[q][1]);
+                    *reinterpret_cast<u32x4*>(&lds_b[buf][lds_chunk(col, (rbk >> 1) + 8 * (rbk & 1))]) =
+                        u32x4{a.x, a.y, b.x, b.y};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CHUNKS; ++i) {
+                const int idx = tid + 256 * i;
+                const int r = idx >> 3, c = idx & 7;
+                u32x4 lo, hi;
+                fp8x16_to_f16(rb[i], lo, hi);
+                *reinterpret_cast<u32x4*>(&lds_b[buf][lds_chunk(r, c)]) = lo;
+                *reinterpret_cast<u32x4*>(&lds_b[buf][lds_chunk(r, c + 8)]) = hi;
+            }
+        }
+        if (tid < BM)
+            lds_sa[buf][tid] = rsa;
+        if constexpr (MODE == Mode::Wgrad) {
+            if (tid >= 128 && tid < 128 + BN)
+                lds_sb[buf][tid - 128] = rsb;
+        }
+    };
+
+    // ------------------------------------------------ main loop
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t nk = G;
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+
+    for (int64_t g = 0; g < nk; ++g) {
+        const int buf = (int)(g & 1);
+        // Prefetch the next group (the last iteration re-reads the final group
+        // instead of branching, which keeps the staging registers in VGPRs).
+        load_global(g + 1 < nk ? g + 1 : g);
+
+        v4f tmp[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                tmp[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v8h fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WTM + i * 16 + lr;
+                fa[i] = *reinterpret_cast<const v8h*>(&lds_a[buf][lds_chunk(row, 4 * s + kg)]);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = wn * WTN + j * 16 + lr;
+                fb[j] = *reinterpret_cast<const v8h*>(&lds_b[buf][lds_chunk(col, 4 * s + kg)]);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], tmp[i][j], 0, 0, 0);
+        }
+
+        // Promotion with this group's scale products.
+        float sbs = 0.f;
+        if constexpr (MODE == Mode::Fwd)
+            sbs = p.sb[(n0 / kGroup) * G + g];
+        else if constexpr (MODE == Mode::Dgrad)
+            sbs = p.sb[g * (p.N / kGroup) + n0 / kGroup];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const v4f sav = *reinterpret_cast<const v4f*>(&lds_sa[buf][wm * WTM + i * 16 + 4 * kg]);
+            if constexpr (MODE == Mode::Wgrad) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const float sbc = lds_sb[buf][wn * WTN + j * 16 + lr];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[i][j][v] = fmaf(tmp[i][j][v], sav[v] * sbc, acc[i][j][v]);
+                }
+            } else {
+                float ps[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    ps[v] = sav[v] * sbs;
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[i][j][v] = fmaf(tmp[i][j][v], ps[v], acc[i][j][v]);
+            }
+        }
+
+        if (g + 1 < nk)
+            store_lds(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ------------------------------------------------ epilogue
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + wn * WTN + j * 16 + lr;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = m0 + wm * WTM + i * 16 + 4 * kg + v;
+                if (row < p.M && col < p.N)
+                    p.c[row * p.N + col] = f32_to_bf16_rne(acc[i][j][v]);
+            }
+        }
+}
+
+// Zeros for an empty contraction (C = 0).  A kernel rather than a memset so
+// the call stays capturable without memset nodes.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ c, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = i; k < n; k += stride)
+        c[k] = 0;
+}
+
+// ================================================================ launchers
+
+template <int BM, int BN, int WM, int WN, Mode MODE>
+static void launch_gemm(GemmArgs p, hipStream_t st)
+{
+    p.tiles_m = (int)((p.M + BM - 1) / BM);
+    p.tiles_n = (int)((p.N + BN - 1) / BN);
+    const unsigned nblocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+    gemm_kernel<BM, BN, WM, WN, MODE><<<nblocks, 256, 0, st>>>(p);
+}
+
+void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st)
+{
+    int64_t b = (n + 255) / 256;
+    if (b > 8192)
+        b = 8192;
+    fill_zero_kernel<<<(unsigned)(b < 1 ? 1 : b), 256, 0, st>>>(static_cast<uint16_t*>(c), n);
+}
+
+void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                     int64_t N, int64_t K, void* y, hipStream_t st)
+{
+    GemmArgs p{xq, sx, wq, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
+    if (M <= 64)
+        launch_gemm<64, 64, 1, 4, Mode::Fwd>(p, st);
+    else
+        launch_gemm<128, 128, 2, 2, Mode::Fwd>(p, st);
+}
+
+void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t T,
+                       int64_t N, int64_t K, void* dx, hipStream_t st)
+{
+    // C = dX [T][K]; contraction over W's rows (N); B(n=k, kc=n) = wq[n][k].
+    GemmArgs p{dyq, sdy, wq, sw, static_cast<uint16_t*>(dx), T, K, N, 0, 0};
+    if (T <= 64)
+        launch_gemm<64, 64, 1, 4, Mode::Dgrad>(p, st);
+    else
+        launch_gemm<128, 128, 2, 2, Mode::Dgrad>(p, st);
+}
+
+void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,
+                       int64_t N, int64_t K, int64_t T, void* dw, hipStream_t st)
+{
+    // C = dW [N][K]; contraction over T.
+    GemmArgs p{dyTq, sdyT, xTq, sxT, static_cast<uint16_t*>(dw), N, K, T, 0, 0};
+    if (N <= 64)
+        launch_gemm<64, 64, 1, 4, Mode::Wgrad>(p, st);
+    else
+        launch_gemm<128, 128, 2, 2, Mode::Wgrad>(p, st);
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,210 @@
+/*
+ * fp8lin.h -- C ABI of libfp8lin, the FP8 block-scaled quantized linear layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the Jet-RL technical summary (gist.science, paper
+ * 2601.14243):
+ *   - section "Quantization scheme": activations are quantized per group of
+ *     1x128, weights per block of 128x128; activations kept for the backward
+ *     pass are stored in FP8; gradients handed between operators stay BF16;
+ *     the backward GEMMs (DGrad and WGrad) run in FP8, WGrad with 1x128 and
+ *     128x1 groupings;
+ *   - section "Core architecture": rollout and the training forward pass use
+ *     one and the same FP8 quantization flow (so both call the functions
+ *     below), with BF16 master weights re-quantized from BF16.
+ * The pages name the format only as "FP8"; this library fixes it as OCP E4M3FN
+ * (max 448), the scale of a group as fp32(amax / 448), codes as
+ * E4M3(fp32(x / scale)) with round-to-nearest-even and saturation, fp32
+ * accumulation with one scale product per 128-wide contraction group, and
+ * BF16 (round-to-nearest-even) GEMM outputs.
+ *
+ * Conventions for every call:
+ *   - All tensors are dense, row-major, on the current HIP device, allocated
+ *     and owned by the caller.  The library allocates nothing, keeps no
+ *     pointer after it returns and has no mutable global state apart from a
+ *     per-device architecture check cached on first use; calls are
+ *     thread-safe.
+ *   - BF16 tensors are passed as void* (2 bytes per element); FP8 codes as
+ *     uint8_t (one E4M3FN code per byte); scales as float.
+ *   - "1x128 scales of an [R,C] tensor" are float [R][C/128]; "128x128 scales"
+ *     are float [R/128][C/128].  Groups are aligned at index 0.
+ *   - The dimension along which 128-groups run must be a multiple of 128;
+ *     other dimensions are free (ragged tails are handled).  Sizes are
+ *     int64_t and must be >= 0.
+ *   - Every base pointer must be 16-byte aligned.  Outputs must not overlap
+ *     inputs or each other.  A required pointer may be NULL only when the
+ *     call has nothing to read or write.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return; there is no host synchronisation.
+ *     Buffers must stay valid until the enqueued work has finished.
+ *   - Errors: argument errors are detected on the host before anything is
+ *     enqueued and the outputs are left untouched.  FP8LIN_ERR_DEVICE means
+ *     the current device is not a gfx950 (or there is none).  FP8LIN_ERR_HIP
+ *     means a HIP runtime call or launch failed; fp8lin_last_hip_error()
+ *     returns that hipError_t for the calling thread.  Nothing aborts or
+ *     throws across this boundary.
+ *   - An all-zero group gets scale 0 and signed-zero codes (0x00 / 0x80).
+ *     Non-finite inputs are outside the contract.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8LIN_VERSION 1
+#define FP8LIN_GROUP 128
+
+typedef enum fp8lin_status {
+    FP8LIN_OK = 0,
+    FP8LIN_ERR_NULL = 1,   /* a required pointer is NULL                          */
+    FP8LIN_ERR_SHAPE = 2,  /* negative size, 128-group dim not a multiple of 128,
+                              or a size whose byte count overflows int64          */
+    FP8LIN_ERR_ALIGN = 3,  /* a base pointer is not 16-byte aligned              */
+    FP8LIN_ERR_ALIAS = 4,  /* an output overlaps an input or another output      */
+    FP8LIN_ERR_DEVICE = 5, /* no HIP device, or the current device is not gfx950 */
+    FP8LIN_ERR_HIP = 6,    /* a HIP call or kernel launch failed                 */
+    FP8LIN_ERR_ARG = 7     /* an enum argument is out of range, or an option is
+                              not available for the chosen source kind           */
+} fp8lin_status;
+
+/* Source kinds of fp8_quant_transpose. */
+typedef enum fp8lin_src_kind {
+    FP8LIN_SRC_BF16 = 0,     /* src is BF16 [T,C]                                       */
+    FP8LIN_SRC_FP8_ROWQ = 1  /* src is E4M3 codes [T,C] with 1x128 scales [T][C/128]:   */
+                             /* the FP8 activations saved by the forward pass           */
+} fp8lin_src_kind;
+
+/* Library version (FP8LIN_VERSION of the build). */
+int fp8lin_version(void);
+
+/* Static, human-readable text for a status value (never NULL). */
+const char* fp8lin_status_string(int status);
+
+/* hipError_t behind the calling thread's most recent FP8LIN_ERR_HIP (0 if none). */
+int fp8lin_last_hip_error(void);
+
+/*
+ * Activation quantization, 1x128 groups (forward, rollout and reference-model
+ * activations; also the output gradient dY before DGrad).
+ * Jet-RL summary, "Quantization scheme": per-group 1x128 activations.
+ *   x   : BF16 [M,K]            (input)
+ *   xq  : uint8 E4M3 [M,K]      (output)
+ *   sx  : float [M][K/128]      (output) sx[m][g] = fp32(max_{k in g}|x[m,k]| / 448)
+ * K % 128 == 0.  M == 0 or K == 0 is an OK no-op.
+ * Rows are independent: quantizing any subset of rows gives identical codes
+ * and scales, which is what keeps rollout and training on one flow.
+ */
+fp8lin_status fp8_quant_act(const void* x, int64_t M, int64_t K,
+                            uint8_t* xq, float* sx, void* stream);
+
+/*
+ * Weight quantization, 128x128 blocks (from the BF16 master weights, once per
+ * optimizer step).  Jet-RL summary, "Quantization scheme" (128x128 per-block
+ * weights) and "Core architecture" (BF16 master weights).
+ *   w   : BF16 [N,K]                (input)
+ *   wq  : uint8 E4M3 [N,K]          (output)
+ *   sw  : float [N/128][K/128]      (output) one scale per block
+ * N % 128 == 0 and K % 128 == 0.  N == 0 or K == 0 is an OK no-op.
+ */
+fp8lin_status fp8_quant_weight(const void* w, int64_t N, int64_t K,
+                               uint8_t* wq, float* sw, void* stream);
+
+/*
+ * Transpose-quantization along tokens, 128x1 groups (WGrad operands).
+ * Jet-RL summary, "Quantization scheme" (WGrad uses 1x128 and 128x1
+ * quantization) and "Implementation" (custom transposition kernels).
+ * For each column c and each run of 128 consecutive rows t, one scale and 128
+ * codes are produced and written transposed, so the outputs are the 1x128
+ * row-group quantization of the transposed tensor:
+ *   kind == FP8LIN_SRC_BF16:
+ *     src        : BF16 [T,C];  src_scales must be NULL
+ *   kind == FP8LIN_SRC_FP8_ROWQ:
+ *     src        : uint8 E4M3 [T,C];  src_scales : float [T][C/128]
+ *     values are first dequantized exactly as v = fp32(dec(src) * scale)
+ *   dstT  : uint8 E4M3 [C,T]      (output)
+ *   sT    : float [C][T/128]      (output)
+ *   dst_rowq, s_rowq : optional second output (both NULL, or both set;
+ *     BF16 source only): the 1x128 activation quantization of src,
+ *     [T,C] codes and [T][C/128] scales, bit-identical to fp8_quant_act on
+ *     src, produced from the same read of src.
+ * T % 128 == 0.  C % 128 == 0 for the FP8 source and for the dual output;
+ * otherwise C >= 0 is free.  T == 0 or C == 0 is an OK no-op.
+ * Returns FP8LIN_ERR_ARG for an unknown kind, a FP8 source with dual output
+ * or with src_scales == NULL, or a BF16 source with src_scales != NULL.
+ */
+fp8lin_status fp8_quant_transpose(int kind, const void* src, const float* src_scales,
+                                  int64_t T, int64_t C,
+                                  uint8_t* dstT, float* sT,
+                                  uint8_t* dst_rowq, float* s_rowq, void* stream);
+
+/*
+ * Forward / rollout GEMM (NT):  Y = X W^T.
+ * Jet-RL summary, "Quantization scheme" and "Core architecture": FP8 GEMM on
+ * 1x128-quantized activations and 128x128-quantized weights, identical for
+ * rollout and training.
+ *   Y[m,n] = sum_g sx[m][g] * sw[n/128][g] * sum_{k in g} dec(xq[m,k]) dec(wq[n,k])
+ *   xq : [M,K], sx : [M][K/128], wq : [N,K], sw : [N/128][K/128]
+ *   y  : BF16 [M,N] (output), fp32 accumulation, round-to-nearest-even.
+ * N % 128 == 0 and K % 128 == 0; M >= 0 is free.  M == 0 or N == 0 is an OK
+ * no-op; K == 0 writes zeros.
+ */
+fp8lin_status fp8_gemm_fwd(const uint8_t* xq, const float* sx,
+                           const uint8_t* wq, const float* sw,
+                           int64_t M, int64_t N, int64_t K,
+                           void* y, void* stream);
+
+/*
+ * DGrad GEMM (NN):  dX = dY W, contracted over W's row dimension N.
+ * Jet-RL summary, "Quantization scheme": the backward DGrad GEMM runs in FP8.
+ *   dX[t,k] = sum_g sdy[t][g] * sw[g][k/128] * sum_{n in g} dec(dyq[t,n]) dec(wq[n,k])
+ *   dyq : [T,N], sdy : [T][N/128] (1x128 quantization of dY, fp8_quant_act),
+ *   wq : [N,K], sw : [N/128][K/128] (the forward's weight quantization)
+ *   dx  : BF16 [T,K] (output).
+ * N % 128 == 0 and K % 128 == 0; T >= 0 is free.  T == 0 or K == 0 is an OK
+ * no-op; N == 0 writes zeros.
+ */
+fp8lin_status fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy,
+                             const uint8_t* wq, const float* sw,
+                             int64_t T, int64_t N, int64_t K,
+                             void* dx, void* stream);
+
+/*
+ * WGrad GEMM (NT over tokens):  dW = dY^T X.
+ * Jet-RL summary, "Quantization scheme": WGrad in FP8 with both operands
+ * grouped 128-along-tokens, which fp8_quant_transpose produces.
+ *   dW[n,k] = sum_g sdyT[n][g] * sxT[k][g] * sum_{t in g} dec(dyTq[n,t]) dec(xTq[k,t])
+ *   dyTq : [N,T], sdyT : [N][T/128], xTq : [K,T], sxT : [K][T/128]
+ *   dw   : BF16 [N,K] (output).
+ * T % 128 == 0; N >= 0 and K >= 0 are free.  N == 0 or K == 0 is an OK no-op;
+ * T == 0 writes zeros.
+ */
+fp8lin_status fp8_gemm_wgrad(const uint8_t* dyTq, const float* sdyT,
+                             const uint8_t* xTq, const float* sxT,
+                             int64_t N, int64_t K, int64_t T,
+                             void* dw, void* stream);
+
+/*
+ * Diagnostics: the device's fp32 -> E4M3 encoder and E4M3 -> fp32 decoder on n
+ * values, so that tests can check them against the definition on every input
+ * (all 2^32 fp32 bit patterns, all 256 codes).
+ *   method 0: the conversion the kernels use;
+ *   method 1: the gfx950 hardware conversion instruction
+ *             (v_cvt_pk_fp8_f32 / v_cvt_pk_f32_fp8), inputs as given;
+ *   method 2: the integer (bit-manipulation) conversion.
+ * The encoders round to nearest even; methods 0 and 2 saturate to +-448 and
+ * keep the input's sign.  NaN/Inf inputs and the NaN codes give unspecified
+ * results.  Buffers are device memory: in/out float [n] and uint8 [n].
+ * FP8LIN_ERR_ARG for a method outside 0..2.
+ */
+fp8lin_status fp8lin_encode_e4m3(const float* in, int64_t n, uint8_t* out, int method, void* stream);
+fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int method, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

@@ -75,6 +75,18 @@ def grad_out(T: int, N: int, seed: int = 0, sigma: float = 1e-3) -> np.ndarray:
     return gaussian_bf16((T, N), sigma, seed, TID_DY)
 
 
+def random_codes(shape, seed: int, tid: int) -> np.ndarray:
+    """Uniform random finite E4M3 codes (the two NaN codes 0x7F/0xFF excluded)."""
+    c = rng(seed, tid).integers(0, 254, size=shape, dtype=np.int64)
+    c = c + (c >= 0x7F)                     # skip 0x7F
+    return c.astype(np.uint8)
+
+
+def random_scales(shape, seed: int, tid: int, lo: float = 1e-3, hi: float = 2e-2) -> np.ndarray:
+    """Positive fp32 scales drawn uniformly from [lo, hi)."""
+    return (lo + (hi - lo) * rng(seed, tid).random(size=shape)).astype(np.float32)
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str

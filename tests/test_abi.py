@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before touching a
+device.  Pointers here are fake addresses: validation never dereferences them,
+and no call reaches a kernel launch (a valid call without a gfx950 device
+returns FP8LIN_ERR_DEVICE)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_block_scaled_act_amd as fl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8lin.h")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, DEVICE, HIP, ARG = range(8)
+HAS_GPU = torch.cuda.is_available()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:fp8lin_status|int|const char\*)\s+(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fp8_block_scaled_act_amd import _build
+    if not os.path.exists(fl.LIB_PATH):
+        _build.build()
+    return fl.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 11, names
+    for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
+              "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+        assert n in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.fp8lin_version() == 1
+
+
+def test_status_strings(L):
+    for s in range(8):
+        t = L.fp8lin_status_string(s).decode()
+        assert t.startswith("FP8LIN_")
+    assert "unknown" in L.fp8lin_status_string(99).decode()
+
+
+def test_product_path_does_not_touch_oracle():
+    """The binding and the library never reference the CPU oracle."""
+    pkg = os.path.join(ROOT, "fp8_block_scaled_act_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                for pat in (r"\bimport\s+oracle", r"\bfrom\s+oracle", r"liboracle", r"\boracle_\w+\s*\(",
+                            r"oracle[/\\]"):
+                    assert not re.search(pat, src), (f, pat)
+
+
+# fake, 16-byte aligned, non-overlapping device addresses; only used where no
+# GPU is visible, so that a validation regression can never launch on them
+A, B, C, D, E, F = (0x10000000 * (i + 1) for i in range(6))
+s0 = ctypes.c_void_p(0)
+fake_ptrs = pytest.mark.skipif(HAS_GPU, reason="fake device addresses are only passed where no GPU exists")
+
+
+@fake_ptrs
+def test_quant_act_validation(L):
+    assert L.fp8_quant_act(A, 4, 100, B, C, s0) == SHAPE            # K not multiple of 128
+    assert L.fp8_quant_act(A, -1, 128, B, C, s0) == SHAPE
+    assert L.fp8_quant_act(None, 4, 128, B, C, s0) == NULL
+    assert L.fp8_quant_act(A, 4, 128, None, C, s0) == NULL
+    assert L.fp8_quant_act(A + 8, 4, 128, B, C, s0) == ALIGN
+    assert L.fp8_quant_act(A, 4, 128, A + 512, C, s0) == ALIAS      # codes overlap input
+    assert L.fp8_quant_act(A, 4, 128, B, B + 256, s0) == ALIAS      # scales overlap codes
+    assert L.fp8_quant_act(A, 2 ** 62, 2 ** 20, B, C, s0) == SHAPE  # byte count overflows
+    # empty: OK without any device and with NULL pointers
+    assert L.fp8_quant_act(None, 0, 256, None, None, s0) == OK
+    assert L.fp8_quant_act(None, 5, 0, None, None, s0) == OK
+
+
+@fake_ptrs
+def test_quant_weight_validation(L):
+    assert L.fp8_quant_weight(A, 128, 100, B, C, s0) == SHAPE
+    assert L.fp8_quant_weight(A, 100, 128, B, C, s0) == SHAPE
+    assert L.fp8_quant_weight(A, 128 * 70000, 128, B, C, s0) == SHAPE   # grid limit
+    assert L.fp8_quant_weight(A, 128, 128, None, C, s0) == NULL
+    assert L.fp8_quant_weight(A, 128, 128, B, A, s0) == ALIAS
+    assert L.fp8_quant_weight(None, 0, 0, None, None, s0) == OK
+
+
+@fake_ptrs
+def test_quant_transpose_validation(L):
+    assert L.fp8_quant_transpose(7, A, None, 128, 128, B, C, None, None, s0) == ARG
+    assert L.fp8_quant_transpose(0, A, D, 128, 128, B, C, None, None, s0) == ARG      # bf16 + scales
+    assert L.fp8_quant_transpose(1, A, D, 128, 128, B, C, E, F, s0) == ARG           # fp8 + dual
+    assert L.fp8_quant_transpose(1, A, None, 128, 128, B, C, None, None, s0) == ARG   # fp8 w/o scales
+    assert L.fp8_quant_transpose(0, A, None, 100, 128, B, C, None, None, s0) == SHAPE
+    assert L.fp8_quant_transpose(1, A, D, 128, 100, B, C, None, None, s0) == SHAPE    # fp8: C % 128
+    assert L.fp8_quant_transpose(0, A, None, 128, 100, B, C, E, F, s0) == SHAPE       # dual: C % 128
+    assert L.fp8_quant_transpose(0, A, None, 128, 128, B, C, E, None, s0) == NULL     # half a dual
+    assert L.fp8_quant_transpose(0, A, None, 128, 128, B, C, B, F, s0) == ALIAS
+    assert L.fp8_quant_transpose(0, A, None, 128, 77, B + 4, C, None, None, s0) == ALIGN
+    assert L.fp8_quant_transpose(0, None, None, 0, 77, None, None, None, None, s0) == OK
+
+
+@fake_ptrs
+def test_gemm_validation(L):
+    assert L.fp8_gemm_fwd(A, B, C, D, 4, 100, 128, E, s0) == SHAPE
+    assert L.fp8_gemm_fwd(A, B, C, D, 4, 128, 100, E, s0) == SHAPE
+    assert L.fp8_gemm_fwd(A, B, None, D, 4, 128, 128, E, s0) == NULL
+    assert L.fp8_gemm_fwd(A, B, C, D, 4, 128, 128, C, s0) == ALIAS
+    assert L.fp8_gemm_fwd(A, B, C, D + 4, 4, 128, 128, E, s0) == ALIGN
+    assert L.fp8_gemm_fwd(None, None, None, None, 0, 128, 128, None, s0) == OK
+    assert L.fp8_gemm_dgrad(A, B, C, D, 4, 100, 128, E, s0) == SHAPE
+    assert L.fp8_gemm_dgrad(A, B, C, D, 4, 128, 100, E, s0) == SHAPE
+    assert L.fp8_gemm_dgrad(None, None, None, None, 0, 128, 128, None, s0) == OK
+    assert L.fp8_gemm_wgrad(A, B, C, D, 5, 7, 100, E, s0) == SHAPE                 # T % 128
+    assert L.fp8_gemm_wgrad(A, B, C, D, 5, 7, 128, A, s0) == ALIAS
+    assert L.fp8_gemm_wgrad(None, None, None, None, 5, 0, 128, None, s0) == OK
+
+
+@fake_ptrs
+def test_diagnostics_validation(L):
+    assert L.fp8lin_encode_e4m3(A, 16, B, 3, s0) == ARG
+    assert L.fp8lin_decode_e4m3(A, -1, B, 0, s0) == SHAPE
+    assert L.fp8lin_encode_e4m3(None, 0, None, 0, s0) == OK
+
+
+@fake_ptrs
+def test_valid_call_without_gpu_reports_device_error(L):
+    assert L.fp8_quant_act(A, 4, 128, B, C, s0) == DEVICE
+    assert L.fp8_gemm_fwd(A, B, C, D, 4, 128, 128, E, s0) == DEVICE
+
+
+def test_binding_raises_on_error(L):
+    with pytest.raises(fl.Fp8LinError, match="FP8LIN_ERR_SHAPE"):
+        fl._check(SHAPE, "x")

@@ -1,0 +1,273 @@
+"""GPU parity of the block-scaled FP8 GEMMs (forward, DGrad, WGrad) against the
+fp64 CPU oracle.  Tolerance (stated by the project's definition of the layer):
+max |C_gpu - C_ref| / (|C_ref| + 0.01 rms(C_ref)) <= 1e-2.  Exactly
+representable cases must match the oracle's bf16 rounding bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_act_amd as fl
+import oracle
+import synthetic
+from gpu_util import DEV, bf16_bits_to_f64, bf16_to_dev, f32_to_dev, host, say, u8_to_dev
+
+pytestmark = pytest.mark.gpu
+G = 128
+TOL = 1e-2
+
+
+def codes_scales(shape_q, shape_s, seed, tid):
+    return synthetic.random_codes(shape_q, seed, tid), synthetic.random_scales(shape_s, seed, tid + 100)
+
+
+def check_metric(y_gpu_bits, ref, what, rms=None):
+    err = oracle.gemm_metric(bf16_bits_to_f64(y_gpu_bits), ref, rms)
+    assert err <= TOL, "%s: metric %.3e > %.0e" % (what, err, TOL)
+    return err
+
+
+# ------------------------------------------------------------------ forward
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (7, 256, 256), (64, 384, 1024), (65, 128, 512),
+                                   (129, 256, 384), (300, 384, 1024), (1000, 256, 256)])
+def test_fwd_random_codes(M, N, K):
+    xq, sx = codes_scales((M, K), (M, K // G), M * 7 + K, 11)
+    wq, sw = codes_scales((N, K), (N // G, K // G), N * 3 + K, 12)
+    say("gemm_fwd", M, N, K)
+    y = fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw))
+    check_metric(host(y), oracle.gemm_fwd(xq, sx, wq, sw), "fwd %dx%dx%d" % (M, N, K))
+
+
+def test_fwd_one_hot_every_code():
+    """Pins MFMA operand decoding and the fragment/output layouts: W holds every
+    finite code once in column 0 of its group; X is one-hot at that column."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    N, K, M = 256, 256, 3
+    wq = np.zeros((N, K), np.uint8)
+    wq[: codes.size, 5] = codes
+    wq[: codes.size, 130] = codes[::-1]
+    sw = np.ones((N // G, K // G), np.float32)
+    xq = np.zeros((M, K), np.uint8)
+    xq[0, 5] = 0x38                               # 1.0
+    xq[1, 130] = 0x38
+    xq[2, 5] = 0x30                               # 0.5
+    sx = np.ones((M, K // G), np.float32)
+    say("gemm_fwd one-hot")
+    y = host(fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw)))
+    ref = oracle.f64_to_bf16(oracle.gemm_fwd(xq, sx, wq, sw))
+    assert np.array_equal(y, ref)
+
+
+def test_fwd_exact_lossless_bitwise():
+    """Lossless-quantizing inputs (E4M3 values x 2^e per group, each group
+    holding +-448 2^e): partial sums are small integers times a power of two,
+    exact in fp32 in any order, so GPU and oracle bf16 bits must agree."""
+    g = np.random.default_rng(5)
+    M, N, K = 96, 256, 512
+    small = oracle.e4m3_decode(np.arange(0x30, 0x48, dtype=np.uint8))     # 0.5 .. 3.75
+    x = g.choice(small, (M, K)) * np.where(g.random((M, K)) < .5, -1, 1)
+    w = g.choice(small, (N, K)) * np.where(g.random((N, K)) < .5, -1, 1)
+    x[:, ::G] = 448.0
+    w[:, ::G] = 448.0
+    xb, wb = synthetic.f32_to_bf16_bits(x), synthetic.f32_to_bf16_bits(w)
+    say("gemm_fwd exact")
+    xq, sx = fl.fp8_quant_act(bf16_to_dev(xb))
+    wq, sw = fl.fp8_quant_weight(bf16_to_dev(wb))
+    y = host(fl.fp8_gemm_fwd(xq, sx, wq, sw))
+    oq, os_ = oracle.quant_act(xb)
+    wq2, sw2 = oracle.quant_weight(wb)
+    ref = oracle.gemm_fwd(oq, os_, wq2, sw2)
+    assert np.array_equal(ref, x @ w.T)
+    assert np.array_equal(y, oracle.f64_to_bf16(ref))
+
+
+def test_fwd_end_to_end_tiny_config():
+    """Forward quantized linear on the tiny config: X [128,1024] ~N(0,1) with 4
+    outlier columns x50, W [1024,1024] ~N(0,0.02): GPU quantizers + GEMM vs the
+    oracle chain."""
+    x = synthetic.activations(128, 1024, seed=0, n_out=4)
+    w = synthetic.weights(1024, 1024, seed=0)
+    say("forward tiny end-to-end")
+    xq, sx = fl.fp8_quant_act(bf16_to_dev(x))
+    wq, sw = fl.fp8_quant_weight(bf16_to_dev(w))
+    y = host(fl.fp8_gemm_fwd(xq, sx, wq, sw))
+    ref = oracle.gemm_fwd(*oracle.quant_act(x), *oracle.quant_weight(w))
+    check_metric(y, ref, "tiny end-to-end")
+
+
+def test_fwd_degenerate():
+    say("gemm_fwd degenerate")
+    e = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
+    wq = u8_to_dev(synthetic.random_codes((128, 256), 0, 1))
+    sw = f32_to_dev(np.ones((1, 2), np.float32))
+    y = fl.fp8_gemm_fwd(e, torch.empty((0, 2), dtype=torch.float32, device=DEV), wq, sw)
+    assert y.shape == (0, 128)
+    xq = torch.empty((5, 0), dtype=torch.uint8, device=DEV)
+    wq0 = torch.empty((128, 0), dtype=torch.uint8, device=DEV)
+    y = fl.fp8_gemm_fwd(xq, torch.empty((5, 0), dtype=torch.float32, device=DEV), wq0,
+                        torch.empty((1, 0), dtype=torch.float32, device=DEV),
+                        out=torch.full((5, 128), 3.0, dtype=torch.bfloat16, device=DEV))
+    assert torch.all(y == 0).item()
+
+
+def test_fwd_power_of_two_scaling_is_exact():
+    """Scaling all X scales by 2^i and all W scales by 2^j scales Y by 2^(i+j)
+    bit for bit (no over/underflow here)."""
+    M, N, K = 130, 256, 512
+    xq, sx = codes_scales((M, K), (M, K // G), 1, 11)
+    wq, sw = codes_scales((N, K), (N // G, K // G), 2, 12)
+    say("gemm_fwd pow2 scaling")
+    y0 = host(fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw)))
+    y1 = host(fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx * 8), u8_to_dev(wq), f32_to_dev(sw / 2)))
+    assert np.array_equal(bf16_bits_to_f64(y1), bf16_bits_to_f64(y0) * 4)
+
+
+def test_fwd_rows_independent_of_batch():
+    """Rows of a 64-row (decode-shaped) call equal the same rows inside a large
+    call bit for bit: one accumulation order for rollout and training."""
+    M, N, K = 512, 256, 1024
+    xq, sx = codes_scales((M, K), (M, K // G), 3, 11)
+    wq, sw = codes_scales((N, K), (N // G, K // G), 4, 12)
+    say("gemm_fwd batch invariance")
+    y_all = host(fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw)))
+    y_64 = host(fl.fp8_gemm_fwd(u8_to_dev(xq[128:192]), f32_to_dev(sx[128:192]), u8_to_dev(wq), f32_to_dev(sw)))
+    y_1 = host(fl.fp8_gemm_fwd(u8_to_dev(xq[300:301]), f32_to_dev(sx[300:301]), u8_to_dev(wq), f32_to_dev(sw)))
+    assert np.array_equal(y_64, y_all[128:192])
+    assert np.array_equal(y_1, y_all[300:301])
+
+
+# -------------------------------------------------------------------- DGrad
+
+@pytest.mark.parametrize("T,N,K", [(1, 128, 128), (7, 256, 128), (64, 384, 256), (129, 256, 384),
+                                   (300, 1024, 256)])
+def test_dgrad_random_codes(T, N, K):
+    dyq, sdy = codes_scales((T, N), (T, N // G), T + N, 21)
+    wq, sw = codes_scales((N, K), (N // G, K // G), N + K, 22)
+    say("gemm_dgrad", T, N, K)
+    dx = fl.fp8_gemm_dgrad(u8_to_dev(dyq), f32_to_dev(sdy), u8_to_dev(wq), f32_to_dev(sw))
+    check_metric(host(dx), oracle.gemm_dgrad(dyq, sdy, wq, sw), "dgrad %dx%dx%d" % (T, N, K))
+
+
+def test_dgrad_permutation_exact():
+    """W = a permutation in 128x128 blocks with power-of-two scales: dX is dY
+    with permuted, rescaled columns, exactly."""
+    g = np.random.default_rng(8)
+    T, N = 200, 256
+    perm = g.permutation(N)
+    wq = np.zeros((N, N), np.uint8)
+    wq[np.arange(N), perm] = 0x38
+    sw = (2.0 ** g.integers(-3, 4, size=(N // G, N // G))).astype(np.float32)
+    dyq = synthetic.random_codes((T, N), 5, 23)
+    sdy = (2.0 ** g.integers(-8, 8, size=(T, N // G))).astype(np.float32)
+    say("gemm_dgrad permutation")
+    dx = host(fl.fp8_gemm_dgrad(u8_to_dev(dyq), f32_to_dev(sdy), u8_to_dev(wq), f32_to_dev(sw)))
+    assert np.array_equal(dx, oracle.f64_to_bf16(oracle.gemm_dgrad(dyq, sdy, wq, sw)))
+
+
+# -------------------------------------------------------------------- WGrad
+
+@pytest.mark.parametrize("N,K,T", [(1, 1, 128), (5, 77, 256), (64, 128, 128), (130, 200, 384),
+                                   (256, 384, 1024)])
+def test_wgrad_random_codes(N, K, T):
+    dyTq, sdyT = codes_scales((N, T), (N, T // G), N + T, 31)
+    xTq, sxT = codes_scales((K, T), (K, T // G), K + T, 32)
+    say("gemm_wgrad", N, K, T)
+    dw = fl.fp8_gemm_wgrad(u8_to_dev(dyTq), f32_to_dev(sdyT), u8_to_dev(xTq), f32_to_dev(sxT))
+    check_metric(host(dw), oracle.gemm_wgrad(dyTq, sdyT, xTq, sxT), "wgrad %dx%dx%d" % (N, K, T))
+
+
+def test_wgrad_swap_roles_transposes():
+    N, K, T = 192, 256, 512
+    a, sa = codes_scales((N, T), (N, T // G), 9, 33)
+    b, sb = codes_scales((K, T), (K, T // G), 10, 34)
+    say("gemm_wgrad swap")
+    d1 = host(fl.fp8_gemm_wgrad(u8_to_dev(a), f32_to_dev(sa), u8_to_dev(b), f32_to_dev(sb)))
+    d2 = host(fl.fp8_gemm_wgrad(u8_to_dev(b), f32_to_dev(sb), u8_to_dev(a), f32_to_dev(sa)))
+    err = oracle.gemm_metric(bf16_bits_to_f64(d2).T, bf16_bits_to_f64(d1))
+    assert err <= TOL
+
+
+def test_backward_end_to_end_small():
+    """The backward flow on the GPU: dY -> dual quant (1x128 rows + 128-along-T
+    transposed), saved FP8 X -> transpose-requant, DGrad and WGrad, against the
+    oracle chain."""
+    T, N, K = 256, 384, 256
+    dy = synthetic.grad_out(T, N, seed=1)
+    x = synthetic.activations(T, K, seed=1, n_out=1)
+    w = synthetic.weights(N, K, seed=1)
+    say("backward end-to-end small")
+    wq, sw = fl.fp8_quant_weight(bf16_to_dev(w))
+    xq, sx = fl.fp8_quant_act(bf16_to_dev(x))
+    dyTq, sdyT, dyq, sdy = fl.fp8_quant_transpose(bf16_to_dev(dy), dual=True)
+    xTq, sxT = fl.fp8_quant_transpose(xq, sx)
+    dx = host(fl.fp8_gemm_dgrad(dyq, sdy, wq, sw))
+    dw = host(fl.fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT))
+    owq, osw = oracle.quant_weight(w)
+    oxq, osx = oracle.quant_act(x)
+    check_metric(dx, oracle.gemm_dgrad(*oracle.quant_act(dy), owq, osw), "dX")
+    check_metric(dw, oracle.gemm_wgrad(*oracle.quant_transpose_bf16(dy), *oracle.quant_transpose_fp8(oxq, osx)),
+                 "dW")
+
+
+# -------------------------------------------- full sizes, sampled rows
+
+def sampled_rows(M, n=12, seed=0):
+    g = np.random.default_rng(seed)
+    rows = set(g.choice(M, size=min(n, M), replace=False).tolist())
+    rows |= {0, M - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name,M,N,K", [("decode 8B up-proj", 64, 14336, 4096),
+                                        ("prefill 7B", 8192, 18944, 3584),
+                                        ("large 32B", 16384, 27648, 5120)])
+def test_fwd_full_size_sampled(name, M, N, K):
+    """Full-size forward (GPU quantizers + GEMM, as timed by the bench), checked
+    on sampled rows that the oracle computes one by one."""
+    x = synthetic.activations(M, K, seed=0)
+    w = synthetic.weights(N, K, seed=0)
+    say("gemm_fwd full", name)
+    xq, sx = fl.fp8_quant_act(bf16_to_dev(x))
+    wq, sw = fl.fp8_quant_weight(bf16_to_dev(w))
+    y = fl.fp8_gemm_fwd(xq, sx, wq, sw)
+    rows = sampled_rows(M)
+    yg = host(y[torch.from_numpy(rows).to(DEV)])
+    del y, xq, sx, wq, sw
+    torch.cuda.empty_cache()
+    oxq, osx = oracle.quant_act(x[rows])
+    owq, osw = oracle.quant_weight(w)
+    ref = oracle.gemm(oracle.dequant_rowgroup(oxq, osx), oracle.dequant_block(owq, osw))
+    check_metric(yg, ref, name)
+
+
+def test_backward_full_size_sampled():
+    """8B-shaped backward (T=8192, N=14336, K=4096): DGrad rows and WGrad rows
+    sampled against the oracle."""
+    T, N, K = 8192, 14336, 4096
+    dy = synthetic.grad_out(T, N, seed=0)
+    x = synthetic.activations(T, K, seed=0)
+    w = synthetic.weights(N, K, seed=0)
+    say("backward full: quantize")
+    wq, sw = fl.fp8_quant_weight(bf16_to_dev(w))
+    xq, sx = fl.fp8_quant_act(bf16_to_dev(x))
+    dyTq, sdyT, dyq, sdy = fl.fp8_quant_transpose(bf16_to_dev(dy), dual=True)
+    xTq, sxT = fl.fp8_quant_transpose(xq, sx)
+    say("backward full: dgrad")
+    dx = fl.fp8_gemm_dgrad(dyq, sdy, wq, sw)
+    say("backward full: wgrad")
+    dw = fl.fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT)
+    rows_t = sampled_rows(T, seed=1)
+    rows_n = sampled_rows(N, seed=2)
+    dxg = host(dx[torch.from_numpy(rows_t).to(DEV)])
+    dwg = host(dw[torch.from_numpy(rows_n).to(DEV)])
+    del dx, dw, wq, sw, xq, sx, dyTq, sdyT, dyq, sdy, xTq, sxT
+    torch.cuda.empty_cache()
+    owq, osw = oracle.quant_weight(w)
+    dyq_o, sdy_o = oracle.quant_act(dy[rows_t])
+    ref_dx = oracle.gemm(oracle.dequant_rowgroup(dyq_o, sdy_o), oracle.dequant_block(owq, osw), b_trans=True)
+    check_metric(dxg, ref_dx, "dgrad full")
+    dyTq_o, sdyT_o = oracle.quant_act(np.ascontiguousarray(dy[:, rows_n].T))
+    oxq, osx = oracle.quant_act(x)
+    xTq_o, sxT_o = oracle.quant_transpose_fp8(oxq, osx)
+    ref_dw = oracle.gemm(oracle.dequant_rowgroup(dyTq_o, sdyT_o), oracle.dequant_rowgroup(xTq_o, sxT_o))
+    check_metric(dwg, ref_dw, "wgrad full")
