@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Throughput of the FP8 block-scaled quantized linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the layer's hot path over one batch of synthetic
+inputs already resident in HBM:
+  decode   (default) 8B-shaped MLP up-proj rollout step: 1x128 quantization of
+           X [64,4096] + block-scaled GEMM against W [14336,4096] quantized
+           128x128 beforehand (as rollout does between optimizer steps);
+           8 weight copies are rotated so the weights come from HBM, not MALL
+  prefill  7B-shaped forward: quantize X [8192,3584] and W [18944,3584], GEMM
+  large    32B-shaped forward: quantize X [16384,5120] and W [27648,5120], GEMM
+  backward 8B-shaped backward: dual transpose-quant of dY [8192,14336],
+           transpose-requant of the saved FP8 X [8192,4096], DGrad and WGrad
+  tiny     X [128,1024], W [1024,1024] (correctness-sized)
+The step is captured once in a HIP graph and replayed; K steps are timed
+between device synchronisations.  value = GEMM TFLOP/s of the whole step.
+
+Also reported, per kernel: the average launch duration from HIP events around
+graph replays of that kernel alone on the same stream, with its algorithmic
+bytes or flops; `roofline` for the dominant kernel; `cpu_baseline`: the CPU
+oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA (the unit the GEMMs run on)
+MALL_BYTES = 256 << 20
+G = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "fp8_block_scaled_act_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ bytes
+
+def act_quant_bytes(rows, cols):
+    return rows * cols * 2 + rows * cols + rows * (cols // G) * 4
+
+
+def weight_quant_bytes(rows, cols):
+    return rows * cols * 2 + rows * cols + (rows // G) * (cols // G) * 4
+
+
+def gemm_bytes(M, N, K, b_scale_elems):
+    return M * K + M * (K // G) * 4 + N * K + b_scale_elems * 4 + 2 * M * N
+
+
+# --------------------------------------------------------------- workloads
+
+class Step:
+    """Kernels of one step: list of (name, launch(i), kind, algorithmic units)."""
+
+    def __init__(self):
+        self.kernels = []
+        self.rotate = 1
+        self.gemm_flop = 0
+        self.config = {}
+
+    def add(self, name, fn, kind, units):
+        self.kernels.append((name, fn, kind, units))
+
+    def run(self, i):
+        for _, fn, _, _ in self.kernels:
+            fn(i)
+
+
+def build_step(name, torch, fl, synthetic):
+    dev = "cuda"
+    wl = synthetic.WORKLOADS[name]
+    st = Step()
+
+    def bf16(bits):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def empty(shape, dtype):
+        return torch.empty(shape, dtype=dtype, device=dev)
+
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    if wl.kind == "forward":
+        M, N, K = wl.M, wl.N, wl.K
+        x = bf16(synthetic.activations(M, K, seed=0, n_out=wl.n_out))
+        w = bf16(synthetic.weights(N, K, seed=0))
+        xq, sx = empty((M, K), u8), empty((M, K // G), f32)
+        y = empty((M, N), bf)
+        if name == "decode":
+            wbytes = N * K
+            st.rotate = max(8, -(-2 * MALL_BYTES // wbytes))
+            wqs = []
+            for r in range(st.rotate):
+                wq, sw = fl.fp8_quant_weight(w)
+                wqs.append((wq, sw))
+            torch.cuda.synchronize()
+            del w
+            st.add("quant_act", lambda i: fl.fp8_quant_act(x, out=(xq, sx)), "hbm", act_quant_bytes(M, K))
+            st.add("gemm_fwd", lambda i: fl.fp8_gemm_fwd(xq, sx, wqs[i % st.rotate][0], wqs[i % st.rotate][1],
+                                                          out=y),
+                   "hbm", gemm_bytes(M, N, K, (N // G) * (K // G)))
+            st.dominant = "gemm_fwd"
+        else:
+            wq, sw = empty((N, K), u8), empty((N // G, K // G), f32)
+            st.add("quant_act", lambda i: fl.fp8_quant_act(x, out=(xq, sx)), "hbm", act_quant_bytes(M, K))
+            st.add("quant_weight", lambda i: fl.fp8_quant_weight(w, out=(wq, sw)), "hbm", weight_quant_bytes(N, K))
+            st.add("gemm_fwd", lambda i: fl.fp8_gemm_fwd(xq, sx, wq, sw, out=y), "mfma", 2 * M * N * K)
+            st.dominant = "gemm_fwd"
+        st.gemm_flop = 2 * M * N * K
+        st.config = {"workload": wl.doc, "M": M, "N": N, "K": K, "outlier_columns": wl.n_out,
+                     "weight_copies_rotated": st.rotate}
+    else:
+        T, N, K = wl.M, wl.N, wl.K
+        dy = bf16(synthetic.grad_out(T, N, seed=0))
+        x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
+        w = bf16(synthetic.weights(N, K, seed=0))
+        wq, sw = fl.fp8_quant_weight(w)              # forward's weight quantization
+        xq, sx = fl.fp8_quant_act(x)                  # saved FP8 activations of the forward
+        torch.cuda.synchronize()
+        del w, x
+        dyTq, sdyT = empty((N, T), u8), empty((N, T // G), f32)
+        dyq, sdy = empty((T, N), u8), empty((T, N // G), f32)
+        xTq, sxT = empty((K, T), u8), empty((K, T // G), f32)
+        dx, dw = empty((T, K), bf), empty((N, K), bf)
+        st.add("quant_transpose_dual_dY",
+               lambda i: fl.fp8_quant_transpose(dy, dual=True, out=(dyTq, sdyT, dyq, sdy)), "hbm",
+               T * N * 2 + 2 * T * N + (N * (T // G) + T * (N // G)) * 4)
+        st.add("quant_transpose_fp8_X", lambda i: fl.fp8_quant_transpose(xq, sx, out=(xTq, sxT, None, None)),
+               "hbm", T * K + T * (K // G) * 4 + T * K + K * (T // G) * 4)
+        st.add("gemm_dgrad", lambda i: fl.fp8_gemm_dgrad(dyq, sdy, wq, sw, out=dx), "mfma", 2 * T * N * K)
+        st.add("gemm_wgrad", lambda i: fl.fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT, out=dw), "mfma", 2 * T * N * K)
+        st.gemm_flop = 4 * T * N * K
+        st.dominant = None
+        st.config = {"workload": wl.doc, "T": T, "N": N, "K": K, "outlier_columns": wl.n_out}
+    return st
+
+
+# ------------------------------------------------------------------ timing
+
+def capture(torch, fns, count):
+    """HIP graph of fns(i) for i in range(count) on a side stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(count):
+            for f in fns:
+                f(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            for f in fns:
+                f(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps):
+    """Average ms per replay, HIP events on the replaying stream."""
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+# ------------------------------------------------------------ cpu baseline
+
+def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    sampled step is repeated until at least min_seconds of CPU time."""
+    import oracle
+    wl = synthetic.WORKLOADS[name]
+    if wl.kind == "forward":
+        M, N, K = wl.M, wl.N, wl.K
+        rows = min(M, 64)
+        x = synthetic.activations(M, K, seed=0, n_out=wl.n_out)[:rows]
+        w = synthetic.weights(N, K, seed=0)
+        wq, sw = oracle.quant_weight(w)
+
+        def work():
+            xq, sx = oracle.quant_act(x)
+            oracle.gemm_fwd(xq, sx, wq, sw)
+        what = ("%d of %d rows of X per repetition: oracle 1x128 quantization + fp64 GEMM against "
+                "the full W (W quantized once, outside the timing)" % (rows, M))
+    else:
+        T, N, K = wl.M, wl.N, wl.K
+        rows = 8
+        dy = synthetic.grad_out(T, N, seed=0)[:rows]
+        w = synthetic.weights(N, K, seed=0)
+        wq, sw = oracle.quant_weight(w)
+
+        def work():
+            dyq, sdy = oracle.quant_act(dy)
+            oracle.gemm_dgrad(dyq, sdy, wq, sw)
+        what = ("DGrad for %d of %d token rows per repetition: oracle 1x128 quantization of the dY "
+                "rows + fp64 GEMM against the full W" % (rows, T))
+    flop = 2 * rows * N * K
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        work()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    return {"value": flop * reps / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%s; %d repetitions" % (what, reps), "seconds": round(dt, 2)}
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_block_scaled_act_amd as fl
+    import synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log("[bench] workload", args.workload, "- building inputs")
+    st = build_step(args.workload, torch, fl, synthetic)
+    R = st.rotate
+    steps = -(-args.steps // R) * R
+    warm = -(-args.warmup // R) * R
+
+    log("[bench] capturing step graph (%d steps per replay)" % R)
+    g_step = capture(torch, [lambda i: st.run(i)], R)
+    for _ in range(warm // R):
+        g_step.replay()
+    torch.cuda.synchronize()
+    log("[bench] timing %d steps" % steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // R):
+        g_step.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    value = st.gemm_flop / (ms_per_step * 1e-3) / 1e12
+
+    log("[bench] per-kernel timing")
+    kernels = {}
+    reps = max(4, min(200, steps // R))
+    for name, fn, kind, units in st.kernels:
+        gk = capture(torch, [fn], R)
+        ms = time_graph(torch, gk, reps) / R
+        if kind == "hbm":
+            ach, unit, peak = units / (ms * 1e-3) / 1e9, "GB/s", HBM_PEAK_GBS
+        else:
+            ach, unit, peak = units / (ms * 1e-3) / 1e12, "TFLOP/s", F16_PEAK_TFLOPS
+        kernels[name] = {"us": round(ms * 1e3, 2), "achieved": round(ach, 1), "unit": unit,
+                         "frac": round(ach / peak, 4), "algorithmic": units}
+        if kind == "mfma":
+            kernels[name]["frac_of_fp8_peak"] = round(ach / FP8_PEAK_TFLOPS, 4)
+        log("[bench]  %-26s %9.2f us  %9.1f %s" % (name, ms * 1e3, ach, unit))
+        del gk
+    dom = st.dominant or max(kernels, key=lambda k: kernels[k]["us"])
+    dk = kernels[dom]
+    kind = [k for (n, _, k, _) in st.kernels if n == dom][0]
+    roofline = {"kernel": dom, "bound": kind, "achieved": dk["achieved"],
+                "peak": HBM_PEAK_GBS if kind == "hbm" else F16_PEAK_TFLOPS, "unit": dk["unit"],
+                "frac": dk["frac"], "traffic": None,
+                "algorithmic_per_launch": dk["algorithmic"], "avg_launch_us": dk["us"]}
+    if kind == "mfma":
+        roofline["peak_note"] = "fp16 MFMA peak: FP8 codes are multiplied exactly on the fp16 matrix core"
+        roofline["frac_of_fp8_peak"] = dk["frac_of_fp8_peak"]
+    traffic_file = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(traffic_file):
+        rec = json.load(open(traffic_file)).get("%s/%s" % (args.workload, dom))
+        if rec and rec.get("source_sha") == source_hash("gemm_kernels.hip", "quant_kernels.hip",
+                                                         "fp8lin_device.hpp"):
+            roofline["traffic"] = rec["bytes_per_launch"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a bounded sample)")
+        cpu = cpu_baseline(args.workload, synthetic)
+        log("[bench]  oracle: %.6f TFLOP/s in %.1f s on %d threads" % (cpu["value"], cpu["seconds"], cpu["cores"]))
+
+    line = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s (% of FP8 MFMA peak); quant GB/s (% HBM)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        "config": st.config, "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
