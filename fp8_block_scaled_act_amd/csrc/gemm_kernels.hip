@@ -31,7 +31,7 @@
 //     permutation of the group applied to both operands, which leaves the
 //     contraction unchanged and lets 8 threads write a row without bank
 //     conflicts.  Chunks are XOR-swizzled with swz(row) so fragment reads of 16
-//     rows hit distinct banks;
+//     rows and staging writes hit distinct banks;
 //   - one group = 4 chained 16x16x32 MFMAs (fp32 C operand, exact fp32 adds);
 //     lane l supplies row (l % 16) and chunk 4 s + l / 16 for step s;
 //     output lane l, register v: row 4 (l / 16) + v, column l % 16.
@@ -63,7 +63,11 @@ struct GemmArgs {
     int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 2)) & 7; }
+// LDS chunk swizzle of a 256-byte row (16 chunks of 16 bytes): a bijection
+// on 16 consecutive rows (fragment reads take one chunk from each of 16 rows
+// per 16-lane group), and rows 2j, 2j+1 map to opposite halves (a 16-lane
+// group of a staging write covers 8 chunks of each of two rows).
+__device__ __forceinline__ int swz(int row) { return ((row & 1) << 3) | ((row >> 1) & 7); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
@@ -73,6 +77,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 }
 
 // 4 E4M3 codes -> 4 fp16 (exact: every E4M3 value is an fp16 value).
+// (v_cvt_scalef32_pk_f16_fp8 does this in two instructions, but measured
+// slower in these kernels than the full-rate pair used here.)
 __device__ __forceinline__ u32x2 fp8x4_to_f16x4(uint32_t w)
 {
     typedef float f2 __attribute__((ext_vector_type(2)));
@@ -194,17 +200,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p)
                 rb[i] = *reinterpret_cast<const u32x4*>(p.b + row * p.Kc + k0 + c * 16);
             }
         }
-        if (tid < BM) {
-            int64_t row = m0 + tid;
+        // Scale loads are unconditional (clamped indices): a load under a
+        // branch makes the wait-count pass drain every outstanding load at
+        // the join, which would serialize the prefetch.
+        {
+            int64_t row = m0 + (tid < BM ? tid : BM - 1);
             row = row < p.M ? row : p.M - 1;
             rsa = p.sa[row * G + g];
         }
         if constexpr (MODE == Mode::Wgrad) {
-            if (tid >= 128 && tid < 128 + BN) {
-                int64_t col = n0 + (tid - 128);
-                col = col < p.N ? col : p.N - 1;
-                rsb = p.sb[col * G + g];
-            }
+            const int t = tid - 128;
+            int64_t col = n0 + (t < 0 ? 0 : (t < BN ? t : BN - 1));
+            col = col < p.N ? col : p.N - 1;
+            rsb = p.sb[col * G + g];
         }
     };
 
@@ -356,6 +364,159 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p)
         }
 }
 
+// =================================================== skinny forward (decode)
+//
+// Rollout decode: at most 64 rows of X against a large W.  The weights are
+// read exactly once and dominate the traffic, so the kernel keeps many
+// weight bytes in flight: each wave owns 16 columns of Y (16 rows of W) and
+// streams its W fragments straight from global memory into a register ring
+// DEPTH groups deep (no LDS), converting them to fp16 in registers.  X is
+// small and L2-resident: the workgroup converts DEPTH groups of it at a time
+// (64 rows x DEPTH*128, fp16) into LDS, so the inner loop over those groups
+// has no barrier and the waves run independently.
+//
+// The vector-memory counter retires loads in order, so waiting for any load
+// also waits for every load issued before it.  Each load is therefore
+// consumed about DEPTH groups after it is issued: W group g is issued while
+// group g - DEPTH is multiplied, and the next X chunk is issued right after
+// the current one has been written to LDS.  No load sits under a branch.
+// DEPTH divides the number of groups.
+//
+// Lane (r, kg) of a wave holds W row n0 + r, bytes [16 kg, 16 kg + 16) and
+// [64 + 16 kg, 64 + 16 kg + 16) of the group (two 64-byte runs per row per
+// load instruction); each MFMA step uses 8 of those 32 codes, and X
+// fragments are read from LDS at the same k positions.
+template <int WAVES, int DEPTH>
+__global__ __launch_bounds__(WAVES * 64) void gemm_fwd_skinny_kernel(const GemmArgs p)
+{
+    constexpr int NT = WAVES * 64;                 // threads
+    constexpr int XCH = 64 * 8 / NT;               // X 16-byte chunks per thread per group
+    static_assert(XCH >= 1, "shape");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_x[DEPTH][64 * 256];
+    __shared__ __attribute__((aligned(16))) float lds_sx[DEPTH][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, kg = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * WAVES) + wave * 16;
+    const int64_t G = p.Kc / kGroup;
+    const uint8_t* wrow = p.b + (n0 + lr) * p.Kc + 16 * kg;
+    const float* swp = p.sb + (n0 / kGroup) * G;
+
+    // X staging: this thread's chunks (rows clamped to M) and scale row
+    const uint8_t* xsrc[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int idx = tid + NT * i;
+        const int r = idx >> 3, c = idx & 7;
+        const int64_t row = r < p.M ? r : p.M - 1;
+        xsrc[i] = p.a + row * p.Kc + c * 16;
+    }
+    const int64_t sr = tid < 64 ? tid : 63;
+    const float* sxsrc = p.sa + (sr < p.M ? sr : p.M - 1) * G;
+
+    u32x4 wring[DEPTH][2];
+    u32x4 xr[DEPTH][XCH];
+    float sxr[DEPTH];
+    auto load_w = [&](int slot, int64_t g) {
+        const int64_t gc = g < G ? g : G - 1;
+        wring[slot][0] = *reinterpret_cast<const u32x4*>(wrow + gc * kGroup);
+        wring[slot][1] = *reinterpret_cast<const u32x4*>(wrow + gc * kGroup + 64);
+    };
+    auto load_xchunk = [&](int64_t g0) {           // groups g0 .. g0 + DEPTH - 1
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int64_t g = g0 + d < G ? g0 + d : G - 1;
+#pragma unroll
+            for (int i = 0; i < XCH; ++i)
+                xr[d][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + g * kGroup);
+            sxr[d] = sxsrc[g];
+        }
+    };
+    auto store_xchunk = [&]() {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+            for (int i = 0; i < XCH; ++i) {
+                const int idx = tid + NT * i;
+                const int r = idx >> 3, c = idx & 7;
+                u32x4 lo, hi;
+                fp8x16_to_f16(xr[d][i], lo, hi);
+                // the permuted group order of gemm_kernel: chunk c, c + 8
+                *reinterpret_cast<u32x4*>(&lds_x[d][lds_chunk(r, c)]) = lo;
+                *reinterpret_cast<u32x4*>(&lds_x[d][lds_chunk(r, c + 8)]) = hi;
+            }
+            if (tid < 64)
+                lds_sx[d][tid] = sxr[d];
+        }
+    };
+
+    // prologue: X chunk 0 and W groups 0..DEPTH-1 in flight
+    load_xchunk(0);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        load_w(d, d);
+
+    v4f acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t g0 = 0; g0 < G; g0 += DEPTH) {
+        __syncthreads();                           // previous chunk fully read
+        store_xchunk();
+        load_xchunk(g0 + DEPTH);
+        __syncthreads();                           // chunk g0 visible
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int64_t g = g0 + d;
+            // W group g from slot d; refill with group g + DEPTH
+            const u32x4 w0 = wring[d][0], w1 = wring[d][1];
+            load_w(d, g + DEPTH);
+            u32x4 wf[4];
+            fp8x16_to_f16(w0, wf[0], wf[1]);
+            fp8x16_to_f16(w1, wf[2], wf[3]);
+
+            v4f tmp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                tmp[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                // Same k sets, in the same step order, as gemm_kernel: step s
+                // of lane group kg takes logical chunk p = 4 s + kg, i.e. k in
+                // [16 (p mod 8) + 8 (p div 8), +8): W fragment (0,2,1,3)[s].
+                // Identical per-output arithmetic makes rows bit-identical
+                // between the decode and the large-tile kernels.
+                const int q = 4 * s + kg;
+                const v8h fb = __builtin_bit_cast(v8h, wf[(s & 1) * 2 + (s >> 1)]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v8h fa = *reinterpret_cast<const v8h*>(&lds_x[d][lds_chunk(16 * i + lr, q)]);
+                    tmp[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, tmp[i], 0, 0, 0);
+                }
+            }
+            const float sw = swp[g];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v4f sav = *reinterpret_cast<const v4f*>(&lds_sx[d][16 * i + 4 * kg]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[i][v] = fmaf(tmp[i][v], sav[v] * sw, acc[i][v]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = 16 * i + 4 * kg + v;
+            if (row < p.M)
+                p.c[row * p.N + n0 + lr] = f32_to_bf16_rne(acc[i][v]);
+        }
+}
+
 // Zeros for an empty contraction (C = 0).  A kernel rather than a memset so
 // the call stays capturable without memset nodes.
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ c, int64_t n)
@@ -389,7 +550,14 @@ void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, cons
                      int64_t N, int64_t K, void* y, hipStream_t st)
 {
     GemmArgs p{xq, sx, wq, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
-    if (M <= 64)
+    const int64_t G = K / kGroup;
+    constexpr int kWaves = 4;
+    const unsigned skinny_grid = (unsigned)(N / (16 * kWaves));
+    if (M <= 64 && G % 8 == 0)
+        gemm_fwd_skinny_kernel<kWaves, 8><<<skinny_grid, kWaves * 64, 0, st>>>(p);
+    else if (M <= 64 && G % 4 == 0)
+        gemm_fwd_skinny_kernel<kWaves, 4><<<skinny_grid, kWaves * 64, 0, st>>>(p);
+    else if (M <= 64)
         launch_gemm<64, 64, 1, 4, Mode::Fwd>(p, st);
     else
         launch_gemm<128, 128, 2, 2, Mode::Fwd>(p, st);
