@@ -234,6 +234,91 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
             "sample": "%s; %d repetitions" % (what, reps), "seconds": round(dt, 2)}
 
 
+# --------------------------------------------------------------- profiling
+#
+# rocprofv3 counter passes need plain (non-graph) dispatches, and the HBM
+# counters are calibrated against a copy of known size:
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o run -- python3 bench.py --workload W --profile-eager
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o run -- python3 bench.py --workload W --profile-eager
+#   python3 bench.py --workload W --ingest-pmc D1/run_counter_collection.csv D2/run_counter_collection.csv
+# The ingest step writes profiles/traffic.json (bytes per launch, scaled by
+# the copy's calibration factor, with the kernel-source hash it belongs to).
+
+CALIB_BYTES = 1 << 30
+PROFILE_REPS = 5
+KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
+    "quant_act": "quant_rowgroup_kernel",
+    "quant_weight": "quant_block_kernel",
+    "quant_transpose_dual_dY": "quant_transpose_bf16_kernel",
+    "quant_transpose_fp8_X": "quant_transpose_fp8_kernel",
+    "gemm_fwd": "gemm_",
+    "gemm_dgrad": "Mode)1",
+    "gemm_wgrad": "Mode)2",
+}
+
+
+def profile_eager(name, torch, fl, synthetic):
+    st = build_step(name, torch, fl, synthetic)
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(PROFILE_REPS):
+        dst.copy_(src)
+    for kname, fn, _, _ in st.kernels:
+        for i in range(PROFILE_REPS):
+            fn(i)
+    torch.cuda.synchronize()
+    log("[bench] profile-eager: %d copies of %d bytes, %d launches of each kernel" %
+        (PROFILE_REPS, CALIB_BYTES, PROFILE_REPS))
+
+
+def ingest_pmc(name, fetch_csv, write_csv, torch, fl, synthetic):
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def avg_kib(table, pred):
+        xs = [v for k, vs in table.items() if pred(k) for v in vs]
+        return sum(xs) / len(xs) if xs else None
+
+    copy_pred = lambda k: "elementwise" in k or "copy" in k.lower()
+    f_copy, w_copy = avg_kib(fetch, copy_pred), avg_kib(write, copy_pred)
+    factor_f = CALIB_BYTES / (f_copy * 1024.0)
+    factor_w = CALIB_BYTES / (w_copy * 1024.0)
+    st = build_step(name, torch, fl, synthetic)
+    sha = source_hash("gemm_kernels.hip", "quant_kernels.hip", "fp8lin_device.hpp")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    for kname, _, kind, units in st.kernels:
+        sym = KERNEL_SYMBOLS[kname]
+        pred = lambda k, sym=sym: sym in k and not copy_pred(k)
+        f, w = avg_kib(fetch, pred), avg_kib(write, pred)
+        if f is None or w is None:
+            continue
+        b = f * 1024.0 * factor_f + w * 1024.0 * factor_w
+        data["%s/%s" % (name, kname)] = {
+            "bytes_per_launch": round(b), "fetch_kib_raw": round(f, 1), "write_kib_raw": round(w, 1),
+            "calibration": {"copy_bytes": CALIB_BYTES, "fetch_factor": round(factor_f, 4),
+                            "write_factor": round(factor_w, 4)},
+            "algorithmic_bytes": units if kind == "hbm" else None,
+            "source_sha": sha,
+        }
+        log("[bench] %s/%s: %.1f MB per launch (fetch %.1f MiB, write %.1f MiB raw)" %
+            (name, kname, b / 1e6, f / 1024, w / 1024))
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+
+
 # -------------------------------------------------------------------- main
 
 def main():
@@ -243,6 +328,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-eager", action="store_true",
+                    help="run each kernel of the step eagerly (for rocprofv3 counter passes) and exit")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -255,6 +344,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.profile_eager:
+        profile_eager(args.workload, torch, fl, synthetic)
+        return
+    if args.ingest_pmc:
+        ingest_pmc(args.workload, args.ingest_pmc[0], args.ingest_pmc[1], torch, fl, synthetic)
+        return
     log("[bench] workload", args.workload, "- building inputs")
     st = build_step(args.workload, torch, fl, synthetic)
     R = st.rotate
