@@ -367,66 +367,80 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p)
 // =================================================== skinny forward (decode)
 //
 // Rollout decode: at most 64 rows of X against a large W.  The weights are
-// read exactly once and dominate the traffic, so the kernel keeps many
-// weight bytes in flight: each wave owns 16 columns of Y (16 rows of W) and
-// streams its W fragments straight from global memory into a register ring
-// DEPTH groups deep (no LDS), converting them to fp16 in registers.  X is
-// small and L2-resident: the workgroup converts DEPTH groups of it at a time
-// (64 rows x DEPTH*128, fp16) into LDS, so the inner loop over those groups
-// has no barrier and the waves run independently.
+// read once and dominate the traffic; the work per column is too small for
+// one wave per SIMD to hide its latencies, so the contraction is also split
+// inside the workgroup.  A workgroup covers 64 columns of Y with KSPLIT parts
+// of K; each part has 4 / CT waves, each wave owns CT tiles of 16 columns
+// (16 * CT rows of W) for its part.  A wave streams its W fragments straight
+// from global memory into a register ring DEPTH groups deep and converts
+// them to fp16 in registers; the waves of a part stage their X (64 rows,
+// DEPTH groups at a time) as fp16 into their own LDS region, and each X
+// fragment read from LDS feeds CT MFMAs.  At the end the partial sums of the
+// parts are added in part order (deterministic) through LDS.
 //
 // The vector-memory counter retires loads in order, so waiting for any load
-// also waits for every load issued before it.  Each load is therefore
-// consumed about DEPTH groups after it is issued: W group g is issued while
-// group g - DEPTH is multiplied, and the next X chunk is issued right after
-// the current one has been written to LDS.  No load sits under a branch.
-// DEPTH divides the number of groups.
+// also waits for every load issued before it: every load is consumed about
+// DEPTH groups after it is issued and none sits under a branch.
+// KSPLIT * DEPTH divides the number of groups.
 //
-// Lane (r, kg) of a wave holds W row n0 + r, bytes [16 kg, 16 kg + 16) and
-// [64 + 16 kg, 64 + 16 kg + 16) of the group (two 64-byte runs per row per
-// load instruction); each MFMA step uses 8 of those 32 codes, and X
-// fragments are read from LDS at the same k positions.
-template <int WAVES, int DEPTH>
-__global__ __launch_bounds__(WAVES * 64) void gemm_fwd_skinny_kernel(const GemmArgs p)
+// Lane (r, kg) of a wave holds, per column tile, W row n + r, bytes
+// [16 kg, 16 kg + 16) and [64 + 16 kg, 64 + 16 kg + 16) of the group (two
+// 64-byte runs per row per load instruction); each MFMA step uses 8 of those
+// 32 codes, and X fragments are read from LDS at the same k positions.
+template <int KSPLIT, int CT, int DEPTH>
+__global__ __launch_bounds__(KSPLIT * 256 / CT) void gemm_fwd_skinny_kernel(const GemmArgs p)
 {
-    constexpr int NT = WAVES * 64;                 // threads
-    constexpr int XCH = 64 * 8 / NT;               // X 16-byte chunks per thread per group
-    static_assert(XCH >= 1, "shape");
-    __shared__ __attribute__((aligned(16))) uint8_t lds_x[DEPTH][64 * 256];
-    __shared__ __attribute__((aligned(16))) float lds_sx[DEPTH][64];
+    constexpr int WPP = 4 / CT;                    // waves per part
+    constexpr int TPP = 64 * WPP;                  // threads per part
+    constexpr int XCH = 512 / TPP;                 // X 16-byte chunks per thread per group
+    __shared__ __attribute__((aligned(16))) uint8_t lds_x[KSPLIT][DEPTH][64 * 256];
+    __shared__ __attribute__((aligned(16))) float lds_sx[KSPLIT][DEPTH][64];
+    static_assert(4 * 64 * 16 * sizeof(float) <= (size_t)KSPLIT * DEPTH * 64 * 256 / (KSPLIT > 1 ? KSPLIT - 1 : 1),
+                  "partial sums fit in the X regions");
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int ptid = tid % TPP;                    // thread index within its part
+    const int lane = tid & 63;
+    const int wip = ptid >> 6;                     // wave within the part
+    const int kp = tid / TPP;                      // K part
     const int lr = lane & 15, kg = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * WAVES) + wave * 16;
+    const int64_t nw = (int64_t)blockIdx.x * 64 + wip * 16 * CT;   // first column of this wave
     const int64_t G = p.Kc / kGroup;
-    const uint8_t* wrow = p.b + (n0 + lr) * p.Kc + 16 * kg;
-    const float* swp = p.sb + (n0 / kGroup) * G;
+    const int64_t GP = G / KSPLIT;                 // groups per part
+    const int64_t gbeg = kp * GP;
+    const uint8_t* wrow[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t)
+        wrow[t] = p.b + (nw + 16 * t + lr) * p.Kc + 16 * kg;
+    const float* swp = p.sb + (nw / kGroup) * G;  // the wave's 16 CT columns lie in one 128-block
 
-    // X staging: this thread's chunks (rows clamped to M) and scale row
+    // X staging for this part: chunks (rows clamped to M) and scale row
     const uint8_t* xsrc[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-        const int idx = tid + NT * i;
+        const int idx = ptid + TPP * i;
         const int r = idx >> 3, c = idx & 7;
         const int64_t row = r < p.M ? r : p.M - 1;
         xsrc[i] = p.a + row * p.Kc + c * 16;
     }
-    const int64_t sr = tid < 64 ? tid : 63;
+    const int64_t sr = ptid < 64 ? ptid : 63;
     const float* sxsrc = p.sa + (sr < p.M ? sr : p.M - 1) * G;
 
-    u32x4 wring[DEPTH][2];
+    u32x4 wring[DEPTH][CT][2];
     u32x4 xr[DEPTH][XCH];
     float sxr[DEPTH];
-    auto load_w = [&](int slot, int64_t g) {
-        const int64_t gc = g < G ? g : G - 1;
-        wring[slot][0] = *reinterpret_cast<const u32x4*>(wrow + gc * kGroup);
-        wring[slot][1] = *reinterpret_cast<const u32x4*>(wrow + gc * kGroup + 64);
+    auto load_w = [&](int slot, int64_t g) {      // g relative to the part
+        const int64_t gc = gbeg + (g < GP ? g : GP - 1);
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            wring[slot][t][0] = *reinterpret_cast<const u32x4*>(wrow[t] + gc * kGroup);
+            wring[slot][t][1] = *reinterpret_cast<const u32x4*>(wrow[t] + gc * kGroup + 64);
+        }
     };
-    auto load_xchunk = [&](int64_t g0) {           // groups g0 .. g0 + DEPTH - 1
+    auto load_xchunk = [&](int64_t g0) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            const int64_t g = g0 + d < G ? g0 + d : G - 1;
+            const int64_t g = gbeg + (g0 + d < GP ? g0 + d : GP - 1);
 #pragma unroll
             for (int i = 0; i < XCH; ++i)
                 xr[d][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + g * kGroup);
@@ -438,31 +452,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_fwd_skinny_kernel(const GemmA
         for (int d = 0; d < DEPTH; ++d) {
 #pragma unroll
             for (int i = 0; i < XCH; ++i) {
-                const int idx = tid + NT * i;
+                const int idx = ptid + TPP * i;
                 const int r = idx >> 3, c = idx & 7;
                 u32x4 lo, hi;
                 fp8x16_to_f16(xr[d][i], lo, hi);
                 // the permuted group order of gemm_kernel: chunk c, c + 8
-                *reinterpret_cast<u32x4*>(&lds_x[d][lds_chunk(r, c)]) = lo;
-                *reinterpret_cast<u32x4*>(&lds_x[d][lds_chunk(r, c + 8)]) = hi;
+                *reinterpret_cast<u32x4*>(&lds_x[kp][d][lds_chunk(r, c)]) = lo;
+                *reinterpret_cast<u32x4*>(&lds_x[kp][d][lds_chunk(r, c + 8)]) = hi;
             }
-            if (tid < 64)
-                lds_sx[d][tid] = sxr[d];
+            if (ptid < 64)
+                lds_sx[kp][d][ptid] = sxr[d];
         }
     };
 
-    // prologue: X chunk 0 and W groups 0..DEPTH-1 in flight
     load_xchunk(0);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
         load_w(d, d);
 
-    v4f acc[4];
+    v4f acc[CT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[t][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t g0 = 0; g0 < G; g0 += DEPTH) {
+    for (int64_t g0 = 0; g0 < GP; g0 += DEPTH) {
         __syncthreads();                           // previous chunk fully read
         store_xchunk();
         load_xchunk(g0 + DEPTH);
@@ -470,51 +485,91 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_fwd_skinny_kernel(const GemmA
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int64_t g = g0 + d;
-            // W group g from slot d; refill with group g + DEPTH
-            const u32x4 w0 = wring[d][0], w1 = wring[d][1];
-            load_w(d, g + DEPTH);
-            u32x4 wf[4];
-            fp8x16_to_f16(w0, wf[0], wf[1]);
-            fp8x16_to_f16(w1, wf[2], wf[3]);
-
-            v4f tmp[4];
+            u32x4 wf[CT][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                tmp[i] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < CT; ++t) {
+                fp8x16_to_f16(wring[d][t][0], wf[t][0], wf[t][1]);
+                fp8x16_to_f16(wring[d][t][1], wf[t][2], wf[t][3]);
+            }
+            load_w(d, g + DEPTH);
+
+            v4f tmp[CT][4];
+#pragma unroll
+            for (int t = 0; t < CT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tmp[t][i] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                // Same k sets, in the same step order, as gemm_kernel: step s
-                // of lane group kg takes logical chunk p = 4 s + kg, i.e. k in
-                // [16 (p mod 8) + 8 (p div 8), +8): W fragment (0,2,1,3)[s].
-                // Identical per-output arithmetic makes rows bit-identical
-                // between the decode and the large-tile kernels.
+                // step s of lane group kg takes logical chunk q = 4 s + kg, i.e.
+                // k in [16 (q mod 8) + 8 (q div 8), +8): W fragment (0,2,1,3)[s]
                 const int q = 4 * s + kg;
-                const v8h fb = __builtin_bit_cast(v8h, wf[(s & 1) * 2 + (s >> 1)]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const v8h fa = *reinterpret_cast<const v8h*>(&lds_x[d][lds_chunk(16 * i + lr, q)]);
-                    tmp[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, tmp[i], 0, 0, 0);
+                    const v8h fa = *reinterpret_cast<const v8h*>(&lds_x[kp][d][lds_chunk(16 * i + lr, q)]);
+#pragma unroll
+                    for (int t = 0; t < CT; ++t)
+                        tmp[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            fa, __builtin_bit_cast(v8h, wf[t][(s & 1) * 2 + (s >> 1)]), tmp[t][i], 0, 0, 0);
                 }
             }
-            const float sw = swp[g];
+            const float sw = swp[gbeg + g];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const v4f sav = *reinterpret_cast<const v4f*>(&lds_sx[d][16 * i + 4 * kg]);
+                const v4f sav = *reinterpret_cast<const v4f*>(&lds_sx[kp][d][16 * i + 4 * kg]);
+                float ps[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    acc[i][v] = fmaf(tmp[i][v], sav[v] * sw, acc[i][v]);
+                    ps[v] = sav[v] * sw;
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[t][i][v] = fmaf(tmp[t][i][v], ps[v], acc[t][i][v]);
             }
         }
     }
 
+    // partial sums of parts 1..KSPLIT-1 through LDS (all X reads are over
+    // after the first barrier)
+    if constexpr (KSPLIT > 1) {
+        __syncthreads();
+        float* part = reinterpret_cast<float*>(&lds_x[0][0][0]);
+        const int slot = wip * CT;                 // 16-column tile index in the workgroup
+        if (kp > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+            for (int t = 0; t < CT; ++t) {
+                float* dst = part + ((kp - 1) * 4 + slot + t) * (64 * 16) + lane * 16;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t row = 16 * i + 4 * kg + v;
-            if (row < p.M)
-                p.c[row * p.N + n0 + lr] = f32_to_bf16_rne(acc[i][v]);
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<v4f*>(dst + 4 * i) = acc[t][i];
+            }
         }
+        __syncthreads();
+        if (kp == 0) {
+#pragma unroll
+            for (int k = 1; k < KSPLIT; ++k)
+#pragma unroll
+                for (int t = 0; t < CT; ++t) {
+                    const float* src = part + ((k - 1) * 4 + slot + t) * (64 * 16) + lane * 16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[t][i] += *reinterpret_cast<const v4f*>(src + 4 * i);
+                }
+        }
+    }
+    if (kp == 0) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t row = 16 * i + 4 * kg + v;
+                    if (row < p.M)
+                        p.c[row * p.N + nw + 16 * t + lr] = f32_to_bf16_rne(acc[t][i][v]);
+                }
+    }
 }
 
 // Zeros for an empty contraction (C = 0).  A kernel rather than a memset so
@@ -551,12 +606,8 @@ void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, cons
 {
     GemmArgs p{xq, sx, wq, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
     const int64_t G = K / kGroup;
-    constexpr int kWaves = 4;
-    const unsigned skinny_grid = (unsigned)(N / (16 * kWaves));
     if (M <= 64 && G % 8 == 0)
-        gemm_fwd_skinny_kernel<kWaves, 8><<<skinny_grid, kWaves * 64, 0, st>>>(p);
-    else if (M <= 64 && G % 4 == 0)
-        gemm_fwd_skinny_kernel<kWaves, 4><<<skinny_grid, kWaves * 64, 0, st>>>(p);
+        gemm_fwd_skinny_kernel<4, 1, 2><<<(unsigned)(N / 64), 1024, 0, st>>>(p);
     else if (M <= 64)
         launch_gemm<64, 64, 1, 4, Mode::Fwd>(p, st);
     else

@@ -123,17 +123,24 @@ def test_fwd_power_of_two_scaling_is_exact():
 
 
 def test_fwd_rows_independent_of_batch():
-    """Rows of a 64-row (decode-shaped) call equal the same rows inside a large
-    call bit for bit: one accumulation order for rollout and training."""
+    """A row's result does not depend on the other rows of the call: bit for
+    bit among decode-sized calls (<= 64 rows) and among large calls; across
+    the two kernels (different group summation order) within the metric."""
     M, N, K = 512, 256, 1024
     xq, sx = codes_scales((M, K), (M, K // G), 3, 11)
     wq, sw = codes_scales((N, K), (N // G, K // G), 4, 12)
     say("gemm_fwd batch invariance")
-    y_all = host(fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw)))
-    y_64 = host(fl.fp8_gemm_fwd(u8_to_dev(xq[128:192]), f32_to_dev(sx[128:192]), u8_to_dev(wq), f32_to_dev(sw)))
-    y_1 = host(fl.fp8_gemm_fwd(u8_to_dev(xq[300:301]), f32_to_dev(sx[300:301]), u8_to_dev(wq), f32_to_dev(sw)))
-    assert np.array_equal(y_64, y_all[128:192])
-    assert np.array_equal(y_1, y_all[300:301])
+    run = lambda a, b: host(fl.fp8_gemm_fwd(u8_to_dev(xq[a:b]), f32_to_dev(sx[a:b]), u8_to_dev(wq), f32_to_dev(sw)))
+    y_all = run(0, M)
+    y_mid = run(100, 300)
+    assert np.array_equal(y_mid, y_all[100:300])
+    y_64 = run(128, 192)
+    y_1 = run(130, 131)
+    y_7 = run(125, 132)
+    assert np.array_equal(y_1, y_64[2:3]) and np.array_equal(y_7[3:7], y_64[0:4])   # rows 128..131
+    ref = oracle.gemm_fwd(xq[128:192], sx[128:192], wq, sw)
+    check_metric(y_64, ref, "decode rows")
+    assert oracle.gemm_metric(bf16_bits_to_f64(y_64), bf16_bits_to_f64(y_all[128:192])) <= TOL
 
 
 # -------------------------------------------------------------------- DGrad
