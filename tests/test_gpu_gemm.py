@@ -38,6 +38,20 @@ def test_fwd_random_codes(M, N, K):
     check_metric(host(y), oracle.gemm_fwd(xq, sx, wq, sw), "fwd %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 128, 512), (17, 256, 1024), (64, 384, 2048), (64, 128, 1536),
+                                   (33, 128, 16384), (64, 256, 15872), (64, 512, 14336), (40, 128, 768),
+                                   (64, 128, 256), (3, 256, 17408)])
+def test_fwd_decode_shapes(M, N, K):
+    """At most 64 rows: the streaming decode kernels (K/128 a multiple of 4 up
+    to 128 groups), the K-split fallback and the generic tile, across group
+    counts on both sides of each kernel's limits."""
+    xq, sx = codes_scales((M, K), (M, K // G), M * 13 + K, 21)
+    wq, sw = codes_scales((N, K), (N // G, K // G), N * 5 + K, 22)
+    say("gemm_fwd decode shape", M, N, K)
+    y = fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw))
+    check_metric(host(y), oracle.gemm_fwd(xq, sx, wq, sw), "fwd %dx%dx%d" % (M, N, K))
+
+
 def test_fwd_one_hot_every_code():
     """Pins MFMA operand decoding and the fragment/output layouts: W holds every
     finite code once in column 0 of its group; X is one-hot at that column."""
