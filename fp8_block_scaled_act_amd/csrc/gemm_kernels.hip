@@ -734,31 +734,8 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
             }
         }
     } else if (wave < 8) {
-        const int sw_i = wave - 4;
         const int t = tid - 256;
-        {
-            // scale products for every group, all loads in flight at once
-            const float* swp = p.sb + (n0 / kGroup) * G;
-            const int nps = 64 * (int)G;
-            float sv[GMAX / 4], wv[GMAX / 4];
-#pragma unroll
-            for (int i = 0; i < GMAX / 4; ++i) {
-                const int idx = min(t + 256 * i, nps - 1);
-                const int row = idx / (int)G, g = idx - row * (int)G;
-                const int64_t xrow = row < p.M ? row : p.M - 1;
-                sv[i] = p.sa[xrow * G + g];
-                wv[i] = swp[g];
-            }
-#pragma unroll
-            for (int i = 0; i < GMAX / 4; ++i) {
-                const int idx = t + 256 * i;
-                if (idx < nps) {
-                    const int row = idx / (int)G, g = idx - row * (int)G;
-                    lds_ps[row * GP + g] = sv[i] * wv[i];
-                }
-            }
-        }
-        // thread t moves 16-byte piece t % 8 of rows t / 8 and t / 8 + 32 of
+        // X: thread t moves 16-byte piece t % 8 of rows t / 8 and t / 8 + 32 of
         // both groups of a chunk; rows past M are clamped (never stored)
         const int c8 = t & 7;
         const uint8_t* xs[2];
@@ -782,10 +759,34 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
                 *reinterpret_cast<v8h*>(&lds_x[buf][u >> 1][x_off(row, 2 * c8 + 1)]) = cvt8(xr[slot][u].z, xr[slot][u].w);
             }
         };
-        (void)sw_i;
 #pragma unroll
         for (int j = 0; j < XD; ++j)
             load(j, j);
+        {
+            // scale products sx[r,g] * sw[g] for every group, eight per thread
+            // per batch with the batch's loads in flight together
+            const float* swp = p.sb + (n0 / kGroup) * G;
+            const int nps = 64 * (int)G;
+            for (int base = 0; base < nps; base += 256 * 8) {
+                float sv[8], wv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int idx = min(base + t + 256 * i, nps - 1);
+                    const int row = idx / (int)G, g = idx - row * (int)G;
+                    const int64_t xrow = row < p.M ? row : p.M - 1;
+                    sv[i] = p.sa[xrow * G + g];
+                    wv[i] = swp[g];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int idx = base + t + 256 * i;
+                    if (idx < nps) {
+                        const int row = idx / (int)G, g = idx - row * (int)G;
+                        lds_ps[row * GP + g] = sv[i] * wv[i];
+                    }
+                }
+            }
+        }
         store(0, 0);
         load(0, XD);
         __syncthreads();
