@@ -132,6 +132,26 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
         s[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = gs.s;
 }
 
+// Transposed code tile in LDS: 128 output rows (columns of the source) x
+// 128 tokens, 16-byte token chunks XOR-swizzled so both the quantizing
+// waves' writes and the row-wise reads spread over the banks.
+__device__ __forceinline__ int ct_off(int r, int tchunk) { return r * 128 + ((tchunk ^ ((r >> 2) & 7)) << 4); }
+
+// Stores the 128x128 code tile to qT rows c0 + r (r < nrows), eight lanes per
+// 128-byte row: every store instruction writes 8 full rows.
+__device__ __forceinline__ void store_code_tile(const uint8_t* ctile, uint8_t* __restrict__ qT, int64_t c0,
+                                                int64_t t0, int64_t T, int64_t nrows)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = (int)threadIdx.x + 256 * i;
+        const int r = idx >> 3, pc = idx & 7;
+        if (r < nrows)
+            *reinterpret_cast<uint4*>(qT + (c0 + r) * T + t0 + 16 * pc) =
+                *reinterpret_cast<const uint4*>(ctile + ct_off(r, pc));
+    }
+}
+
 // ==================================================== transpose, BF16 source
 //
 // Tile of 128 tokens (t) x 128 columns (c); one workgroup of 256 threads.
@@ -141,8 +161,8 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
 // tokens and each lane a pair of adjacent columns: reading a tile row is 64
 // consecutive dwords (no bank conflicts), the per-column amax over the
 // wave's 32 tokens is a packed u16 max, the four waves combine through LDS,
-// and each lane writes 32 contiguous codes per column of the transposed
-// output.  RAGGED handles a last column tile with C % 128 != 0 (element-wise
+// and each lane parks 32 codes per column in an LDS code tile that is then
+// written out eight lanes per 128-byte output row.  RAGGED handles a last column tile with C % 128 != 0 (element-wise
 // loads when rows are not 16-byte aligned); out-of-range columns read as 0 and
 // are never written.
 template <bool DUAL, bool RAGGED>
@@ -155,6 +175,7 @@ __global__ __launch_bounds__(256) void quant_transpose_bf16_kernel(const uint16_
 {
     __shared__ uint4 tile[128 * 16];          // [row][16 chunks of 8 bf16] = 32 KB
     __shared__ uint32_t red[4 * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t ctile[128 * 128];
     const int tid = threadIdx.x;
     const int64_t t0 = (int64_t)blockIdx.y * kGroup;
     const int64_t c0 = (int64_t)blockIdx.x * kGroup;
@@ -228,14 +249,14 @@ __global__ __launch_bounds__(256) void quant_transpose_bf16_kernel(const uint16_
         for (int i = 0; i < 32; ++i)
             xv[i] = half ? bf16_hi(d[i]) : bf16_lo(d[i]);
         quantize_n<32>(xv, half ? g1 : g0, codes);
-        if (!RAGGED || c < C) {
-            uint4* dst = reinterpret_cast<uint4*>(qT + c * T + t0 + wave * 32);
-            dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-            dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
-            if (wave == 0)
-                sT[c * GT + blockIdx.y] = half ? g1.s : g0.s;
-        }
+        const int r = 2 * cp + half;
+        *reinterpret_cast<uint4*>(&ctile[ct_off(r, 2 * wave)]) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+        *reinterpret_cast<uint4*>(&ctile[ct_off(r, 2 * wave + 1)]) = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+        if (wave == 0 && (!RAGGED || c < C))
+            sT[c * GT + blockIdx.y] = half ? g1.s : g0.s;
     }
+    __syncthreads();
+    store_code_tile(ctile, qT, c0, t0, T, RAGGED ? (C - c0 < 128 ? C - c0 : 128) : 128);
 }
 
 // ============================================ transpose, saved FP8 source
@@ -245,7 +266,7 @@ __global__ __launch_bounds__(256) void quant_transpose_bf16_kernel(const uint16_
 // values are first dequantized exactly, v = fp32(dec(code) * row scale),
 // then quantized 128-along-tokens as above.  Phase 2: wave = 32 tokens,
 // lane = (column quad, half of the wave's tokens); quad reads are 32
-// consecutive dwords per row.
+// consecutive dwords per row.  Codes leave through the same LDS code tile.
 __global__ __launch_bounds__(256) void quant_transpose_fp8_kernel(const uint8_t* __restrict__ src,
                                                                   const float* __restrict__ srow,
                                                                   int64_t T, int64_t C,
@@ -256,6 +277,7 @@ __global__ __launch_bounds__(256) void quant_transpose_fp8_kernel(const uint8_t*
     __shared__ uint32_t tile[128 * kPitch];
     __shared__ float rs[128];
     __shared__ uint32_t red[8 * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t ctile[128 * 128];
     const int tid = threadIdx.x;
     const int64_t t0 = (int64_t)blockIdx.y * kGroup;
     const int64_t c0 = (int64_t)blockIdx.x * kGroup;
@@ -319,10 +341,12 @@ __global__ __launch_bounds__(256) void quant_transpose_fp8_kernel(const uint8_t*
         uint32_t codes[4];
         quantize_n<16>(v[j], gs, codes);
         const int64_t c = c0 + quad * 4 + j;
-        *reinterpret_cast<uint4*>(qT + c * T + t0 + rbase) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+        *reinterpret_cast<uint4*>(&ctile[ct_off(quad * 4 + j, rbase >> 4)]) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
         if (wave == 0 && half == 0)
             sT[c * GT + blockIdx.y] = gs.s;
     }
+    __syncthreads();
+    store_code_tile(ctile, qT, c0, t0, T, 128);
 }
 
 // ============================================================= diagnostics
