@@ -579,52 +579,56 @@ __global__ __launch_bounds__(KSPLIT * 256 / CT) void gemm_fwd_skinny_kernel(cons
     }
 }
 
-// ====================================== decode forward, W streamed by LDS DMA
+// ===================================== decode forward, operands streamed by LDS DMA
 //
 // Rollout decode with K up to 16384: the same product for at most 64 rows of
 // X, built so that the weight stream never waits for arithmetic.  A
-// workgroup owns 64 columns of Y (64 rows of W) and runs three kinds of
-// waves, synchronised once per chunk of two groups by a workgroup barrier:
-//  * wave 8 streams W with global_load_lds_dwordx4 (each lane's 16 bytes land
-//    at M0 + 16 * lane): one instruction moves four rows x 256 contiguous
-//    bytes (one chunk of a row) into a WD-deep LDS ring.  The instruction is
-//    issued from inline assembly so that the compiler does not drain the
-//    vector-memory counter at every barrier; the wave waits explicitly for
-//    the chunk it is about to publish (vmcnt counts these loads in order).
-//  * waves 4-7 precompute every scale product sx[r,g] * sw[g] once (the 64
-//    columns lie in one 128-column block, so sw is per group only), then
-//    stage X: FP8 codes loaded XD chunks ahead (eight lanes per 128-byte
-//    line), converted exactly to fp16 and written to an LDS double buffer.
-//  * waves 0-3 multiply on v_mfma_f32_32x32x16_f16: wave (ct, kp) owns W rows
-//    [32 ct, +32) on the MFMA M side and all 64 X rows (two 32-row tiles on
-//    the N side) for group kp of every chunk; W codes are converted in
-//    registers with v_cvt_scalef32_pk_f16_fp8 (scale 1: exact).  The two K
-//    parts are added in a fixed order at the end.
+// workgroup owns 64 columns of Y (64 rows of W); both operands travel from
+// global memory into LDS rings by DMA and are converted to fp16 only as MFMA
+// fragments.  One workgroup barrier per chunk of two groups publishes the
+// next chunk and retires the oldest.
+//  * wave 8 streams W, wave 9 streams X (rows past M read row M - 1; their
+//    outputs are never stored) with global_load_lds_dwordx4: each lane's 16
+//    bytes land at M0 + 16 * lane, one instruction moves four rows x 256
+//    contiguous bytes (one chunk of a row).  The W ring is WDW chunks deep,
+//    the X ring WDX (X is an L2 hit).  The instruction is issued from inline
+//    assembly so that the compiler does not drain the vector-memory counter
+//    at every barrier; each loader waits explicitly for the chunk it is about
+//    to publish (vmcnt retires these loads in order).
+//  * waves 0-7 (two per SIMD) first build every scale product sx[r,g]*sw[g]
+//    (the 64 columns lie in one 128-column weight block, so sw is per group
+//    only), then multiply on v_mfma_f32_32x32x16_f16: wave (ct, kp, kq) owns
+//    W rows [32 ct, +32) on the MFMA M side and all 64 X rows (two 32-row
+//    tiles on the N side) for k steps [4 kq, +4) of group kp of every chunk.
+//    Codes are converted with v_cvt_scalef32_pk_f16_fp8 (scale 1: exact);
+//    each W code is converted once, each X code twice (both column halves).
+//    The four (kp, kq) partial sums are added in a fixed order at the end.
 // Lane (m, kh) of a 32x32x16 step st holds k in [64 kh + 8 st, +8) of the
 // group for both operands (a fixed permutation of the group, applied to both
 // sides).  Output lane l holds X row l % 32 of its tile and W rows
 // 8 (j / 4) + 4 (l / 32) + j % 4, j < 16, so each lane needs one scale
 // product per tile and group.
 //
-// LDS layouts (16-byte pieces, rows of a 16-row stripe hit distinct banks):
-//   W chunk: rows in 1 KB blocks of four; piece q of row r at
-//            (r / 4) * 1024 + 16 * (16 (r % 4) + (q ^ (r % 16)));
-//   X group: row r at r * 256, fp16 chunk ch at 16 * (ch ^ (r % 16)).
+// LDS layout of a chunk of either operand (16-byte pieces; the rows of a
+// 16-row stripe hit distinct banks): rows in 1 KB blocks of four, piece q of
+// row r at (r / 4) * 1024 + 16 * (16 (r % 4) + (q ^ (r % 16))).
 namespace dec {
 constexpr int CH = 2;                              // groups per chunk
-constexpr int GMAX = 128;                          // groups covered by the scale table (K <= 16384)
-constexpr int WCH = 64 * CH * kGroup;              // W bytes per chunk
+constexpr int WCH = 64 * CH * kGroup;              // bytes per chunk of one operand
 
 __device__ __forceinline__ void dma16(uint32_t lds, const void* g)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+    // the LDS address is wave-uniform; readfirstlane keeps it in an SGPR for M0
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
+                     __builtin_amdgcn_readfirstlane(lds)),
+                 "v"(g)
+                 : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm()
 {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ int x_off(int r, int ch) { return r * 256 + ((ch ^ (r & 15)) << 4); }
 __device__ __forceinline__ int w_off(int r, int q) { return (r >> 2) * 1024 + ((((r & 3) << 4) | (q ^ (r & 15))) << 4); }
 
 // 8 codes (two words) -> 8 fp16, exact (scale 1.0)
@@ -637,19 +641,57 @@ __device__ __forceinline__ v8h cvt8(uint32_t a, uint32_t b)
     const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b, 1.0f, true);
     return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
+
+// One loader wave: streams the 64 rows [row0, row0 + 64) of a [rows][K]
+// FP8 operand (rows past `rows` read row rows - 1) chunk by chunk into a
+// D-deep LDS ring at `base`, publishing chunk c + 1 at the barrier that
+// ends chunk c.  Passes 3 + nch barriers, like the MMA waves.
+template <int D>
+__device__ __forceinline__ void stream_operand(const uint8_t* src, int64_t rows, int64_t row0, int64_t Kc,
+                                               int64_t nch, uint32_t base, int lane)
+{
+    const int lr4 = lane >> 4, x = lane & 15;
+    const uint8_t* rp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t r = row0 + 4 * i + lr4;
+        rp[i] = src + (r < rows ? r : rows - 1) * Kc + 16 * (x ^ ((4 * i + lr4) & 15));
+    }
+    auto chunk = [&](int64_t c, int slot) {
+        const int64_t cc = c < nch ? c : nch - 1;  // past the end: a harmless re-read
+        const uint32_t dst = base + (uint32_t)(slot * WCH);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            dma16(dst + i * 1024, rp[i] + cc * (CH * kGroup));
+    };
+#pragma unroll
+    for (int c = 0; c < D - 1; ++c)
+        chunk(c, c);
+    wait_vm<(D - 2) * 16>();                       // chunk 0 landed
+    __syncthreads();
+    for (int64_t c = 0; c < nch; ++c) {
+        chunk(c + D - 1, (int)((c + D - 1) % D));  // into the slot drained before the last barrier
+        wait_vm<(D - 2) * 16>();                   // chunk c + 1 landed
+        __syncthreads();
+    }
+    wait_vm<0>();                                  // no DMA may outlive the loop
+    __syncthreads();
+    __syncthreads();
+}
 }  // namespace dec
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// Requires M <= 64, G = K / 128 a multiple of 4 (an even number of chunks:
-// every role passes 2 + G / 2 barriers) and G <= dec::GMAX.
-template <int WD, int XD>
-__global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
+// Requires M <= 64, G = K / 128 even and G <= GM; every role passes
+// 3 + G / 2 barriers.
+template <int WDW, int WDX, int GM>
+__global__ __launch_bounds__(640) void gemm_fwd_decode_kernel(const GemmArgs p)
 {
     using namespace dec;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_w[WD][WCH];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_x[2][CH][64 * 256];
-    __shared__ __attribute__((aligned(16))) float lds_ps[64 * (GMAX + 1)];
+    static_assert(WDX * WCH >= 3 * 2 * 2 * 16 * 64 * 4, "partial sums fit in the X ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_w[WDW][WCH];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_x[WDX][WCH];
+    __shared__ __attribute__((aligned(16))) float lds_ps[64 * (GM + 1)];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -657,8 +699,32 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
     const int GP = (int)G | 1;                     // scale-table row stride (odd: no bank conflicts)
     const int64_t n0 = (int64_t)blockIdx.x * 64;
 
-    if (wave < 4) {
-        const int ct = wave & 1, kp = wave >> 1;
+    if (wave < 8) {
+        {
+            // scale products, four per thread per batch with the batch's loads in flight together
+            const float* swp = p.sb + (n0 / kGroup) * G;
+            const int nps = 64 * (int)G;
+            for (int base = 0; base < nps; base += 512 * 4) {
+                float sv[4], wv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = min(base + tid + 512 * i, nps - 1);
+                    const int row = idx / (int)G, g = idx - row * (int)G;
+                    const int64_t xrow = row < p.M ? row : p.M - 1;
+                    sv[i] = p.sa[xrow * G + g];
+                    wv[i] = swp[g];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = base + tid + 512 * i;
+                    if (idx < nps) {
+                        const int row = idx / (int)G, g = idx - row * (int)G;
+                        lds_ps[row * GP + g] = sv[i] * wv[i];
+                    }
+                }
+            }
+        }
+        const int ct = wave & 1, kp = (wave >> 1) & 1, kq = wave >> 2;
         const int m = lane & 31, kh = lane >> 5;
         const int wr = 32 * ct + m;
         v16f acc[2];
@@ -667,14 +733,19 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[xt][r] = 0.f;
-        __syncthreads();                           // chunk 0 published
+        __syncthreads();                           // chunk 0 of both operands landed, table built
         for (int64_t c = 0; c < nch; ++c) {
-            const uint8_t* wl = lds_w[c % WD];
-            const int xb = (int)(c & 1);
-            u32x4 wv[4];
+            const uint8_t* wl = lds_w[c % WDW];
+            const uint8_t* xl = lds_x[c % WDX];
+            u32x4 wv[2], xv[2][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                wv[q] = *reinterpret_cast<const u32x4*>(wl + w_off(wr, 8 * kp + 4 * kh + q));
+            for (int q = 0; q < 2; ++q) {
+                const int pc = 8 * kp + 4 * kh + 2 * kq + q;
+                wv[q] = *reinterpret_cast<const u32x4*>(wl + w_off(wr, pc));
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt)
+                    xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, pc));
+            }
             v16f tmp[2];
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt)
@@ -682,16 +753,13 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
                 for (int r = 0; r < 16; ++r)
                     tmp[xt][r] = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v8h lo = cvt8(wv[q].x, wv[q].y), hi = cvt8(wv[q].z, wv[q].w);
+            for (int q = 0; q < 2; ++q) {
+                const v8h wlo = cvt8(wv[q].x, wv[q].y), whi = cvt8(wv[q].z, wv[q].w);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int st = 2 * q + h;
-#pragma unroll
-                    for (int xt = 0; xt < 2; ++xt) {
-                        const v8h b = *reinterpret_cast<const v8h*>(&lds_x[xb][kp][x_off(32 * xt + m, 8 * kh + st)]);
-                        tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(h ? hi : lo, b, tmp[xt], 0, 0, 0);
-                    }
+                for (int xt = 0; xt < 2; ++xt) {
+                    const v8h xlo = cvt8(xv[xt][q].x, xv[xt][q].y), xhi = cvt8(xv[xt][q].z, xv[xt][q].w);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wlo, xlo, tmp[xt], 0, 0, 0);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(whi, xhi, tmp[xt], 0, 0, 0);
                 }
             }
 #pragma unroll
@@ -701,22 +769,28 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
                 for (int r = 0; r < 16; ++r)
                     acc[xt][r] = fmaf(tmp[xt][r], sc, acc[xt][r]);
             }
-            __syncthreads();                       // chunk c drained, chunk c + 1 published
+            __syncthreads();                       // chunk c drained, chunk c + 1 landed
         }
-        // K part 1 hands its sums to part 0 through the (now idle) X buffer
-        float* red = reinterpret_cast<float*>(&lds_x[0][0][0]);
-        if (kp == 1) {
+        __syncthreads();                           // both loaders drained: the X ring is idle
+        float* red = reinterpret_cast<float*>(&lds_x[0][0]);
+        const int part = kp * 2 + kq;
+        if (part != 0) {
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    red[((ct * 2 + xt) * 16 + r) * 64 + lane] = acc[xt][r];
+                    red[(((part - 1) * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane] = acc[xt][r];
         }
         __syncthreads();
-        if (kp == 0) {
+        if (part == 0) {
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt) {
                 const int64_t row = 32 * xt + m;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int pp = 0; pp < 3; ++pp)
+                        acc[xt][r] += red[((pp * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane];
                 if (row < p.M) {
 #pragma unroll
                     for (int a4 = 0; a4 < 4; ++a4) {
@@ -724,106 +798,18 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_kernel(const GemmArgs p)
 #pragma unroll
                         for (int b2 = 0; b2 < 2; ++b2) {
                             const int r0 = 4 * a4 + 2 * b2;
-                            const float f0 = acc[xt][r0] + red[((ct * 2 + xt) * 16 + r0) * 64 + lane];
-                            const float f1 = acc[xt][r0 + 1] + red[((ct * 2 + xt) * 16 + r0 + 1) * 64 + lane];
-                            v[b2] = (uint32_t)f32_to_bf16_rne(f0) | ((uint32_t)f32_to_bf16_rne(f1) << 16);
+                            v[b2] = (uint32_t)f32_to_bf16_rne(acc[xt][r0]) |
+                                    ((uint32_t)f32_to_bf16_rne(acc[xt][r0 + 1]) << 16);
                         }
                         *reinterpret_cast<u32x2*>(p.c + row * p.N + n0 + 32 * ct + 8 * a4 + 4 * kh) = u32x2{v[0], v[1]};
                     }
                 }
             }
         }
-    } else if (wave < 8) {
-        const int t = tid - 256;
-        // X: thread t moves 16-byte piece t % 8 of rows t / 8 and t / 8 + 32 of
-        // both groups of a chunk; rows past M are clamped (never stored)
-        const int c8 = t & 7;
-        const uint8_t* xs[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = (t >> 3) + 32 * h;
-            xs[h] = p.a + (int64_t)(row < p.M ? row : p.M - 1) * p.Kc + 16 * c8;
-        }
-        u32x4 xr[XD][4];
-        auto load = [&](int slot, int64_t c) {
-            const int64_t cc = c < nch ? c : nch - 1;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                xr[slot][u] = *reinterpret_cast<const u32x4*>(xs[u & 1] + (cc * CH + (u >> 1)) * kGroup);
-        };
-        auto store = [&](int slot, int buf) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int row = (t >> 3) + 32 * (u & 1);
-                *reinterpret_cast<v8h*>(&lds_x[buf][u >> 1][x_off(row, 2 * c8)]) = cvt8(xr[slot][u].x, xr[slot][u].y);
-                *reinterpret_cast<v8h*>(&lds_x[buf][u >> 1][x_off(row, 2 * c8 + 1)]) = cvt8(xr[slot][u].z, xr[slot][u].w);
-            }
-        };
-#pragma unroll
-        for (int j = 0; j < XD; ++j)
-            load(j, j);
-        {
-            // scale products sx[r,g] * sw[g] for every group, eight per thread
-            // per batch with the batch's loads in flight together
-            const float* swp = p.sb + (n0 / kGroup) * G;
-            const int nps = 64 * (int)G;
-            for (int base = 0; base < nps; base += 256 * 8) {
-                float sv[8], wv[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int idx = min(base + t + 256 * i, nps - 1);
-                    const int row = idx / (int)G, g = idx - row * (int)G;
-                    const int64_t xrow = row < p.M ? row : p.M - 1;
-                    sv[i] = p.sa[xrow * G + g];
-                    wv[i] = swp[g];
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int idx = base + t + 256 * i;
-                    if (idx < nps) {
-                        const int row = idx / (int)G, g = idx - row * (int)G;
-                        lds_ps[row * GP + g] = sv[i] * wv[i];
-                    }
-                }
-            }
-        }
-        store(0, 0);
-        load(0, XD);
-        __syncthreads();
-        for (int64_t c0 = 0; c0 < nch; c0 += 2) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                // chunk c0 + h + 1 into the buffer drained before the last barrier
-                store((h + 1) % XD, (h + 1) & 1);
-                load((h + 1) % XD, c0 + h + 1 + XD);
-                __syncthreads();
-            }
-        }
-        __syncthreads();
+    } else if (wave == 8) {
+        stream_operand<WDW>(p.b, p.N, n0, p.Kc, nch, (uint32_t)(uintptr_t)&lds_w[0][0], lane);
     } else {
-        const uint32_t wbase = (uint32_t)(uintptr_t)&lds_w[0][0];
-        const int lr4 = lane >> 4, x = lane & 15;
-        auto dma_chunk = [&](int64_t c) {
-            const int64_t cc = c < nch ? c : nch - 1;  // past the end: a harmless re-read
-            const uint32_t dst = wbase + (uint32_t)((c % WD) * WCH);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 4 * i + lr4;
-                dma16(dst + i * 1024, p.b + (n0 + r) * p.Kc + cc * (CH * kGroup) + 16 * (x ^ (r & 15)));
-            }
-        };
-#pragma unroll
-        for (int c = 0; c < WD - 1; ++c)
-            dma_chunk(c);
-        wait_vm<(WD - 2) * 16>();                  // chunk 0 landed
-        __syncthreads();
-        for (int64_t c = 0; c < nch; ++c) {
-            dma_chunk(c + WD - 1);                 // into the slot drained before the last barrier
-            wait_vm<(WD - 2) * 16>();              // chunk c + 1 landed
-            __syncthreads();
-        }
-        wait_vm<0>();                              // no DMA may outlive the workgroup
-        __syncthreads();
+        stream_operand<WDX>(p.a, p.M, 0, p.Kc, nch, (uint32_t)(uintptr_t)&lds_x[0][0], lane);
     }
 }
 
@@ -861,8 +847,10 @@ void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, cons
 {
     GemmArgs p{xq, sx, wq, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
     const int64_t G = K / kGroup;
-    if (M <= 64 && G % 4 == 0 && G <= dec::GMAX)
-        gemm_fwd_decode_kernel<3, 2><<<(unsigned)(N / 64), 576, 0, st>>>(p);
+    if (M <= 64 && G % 2 == 0 && G <= 64)
+        gemm_fwd_decode_kernel<3, 4, 64><<<(unsigned)(N / 64), 640, 0, st>>>(p);
+    else if (M <= 64 && G % 2 == 0 && G <= 128)
+        gemm_fwd_decode_kernel<3, 4, 128><<<(unsigned)(N / 64), 640, 0, st>>>(p);
     else if (M <= 64 && G % 8 == 0)
         gemm_fwd_skinny_kernel<4, 1, 2><<<(unsigned)(N / 64), 1024, 0, st>>>(p);
     else if (M <= 64)
