@@ -170,6 +170,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs p)
     u32x4 rb[MODE == Mode::Dgrad ? 1 : B_CHUNKS];
     uint32_t rbd[MODE == Mode::Dgrad ? DG_ROWS : 1];
     float rsa = 0.f, rsb = 0.f;
+    float rsbs = 1.f;                               // Fwd/Dgrad: the group's W-block scale
 
     auto load_global = [&](int64_t g) {
         const int64_t k0 = g * kGroup;
@@ -211,6 +212,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs p)
             int64_t col = n0 + (t < 0 ? 0 : (t < BN ? t : BN - 1));
             col = col < p.N ? col : p.N - 1;
             rsb = p.sb[col * G + g];
+        } else if constexpr (MODE == Mode::Fwd) {
+            rsbs = p.sb[(n0 / kGroup) * G + g];
+        } else {
+            rsbs = p.sb[g * (p.N / kGroup) + n0 / kGroup];
         }
     };
 
@@ -224,8 +229,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs p)
             *reinterpret_cast<u32x4*>(&lds_a[buf][lds_chunk(r, c)]) = lo;
             *reinterpret_cast<u32x4*>(&lds_a[buf][lds_chunk(r, c + 8)]) = hi;
         }
+        // Fwd/Dgrad: the row scale times the group's W-block scale, i.e. the
+        // whole promotion factor of the row (one fp32 product, as before)
         if (tid < BM)
-            lds_sa[buf][tid] = rsa;
+            lds_sa[buf][tid] = MODE == Mode::Wgrad ? rsa : rsa * rsbs;
     };
     auto store_b = [&](int buf) {
         if constexpr (MODE == Mode::Dgrad) {
@@ -288,72 +295,77 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs p)
     load_global(nk > 1 ? 1 : 0);
     __syncthreads();
 
-    for (int64_t g = 0; g < nk; ++g) {
-        const int buf = (int)(g & 1);
-        v4f tmp[TM][TN];
+    // fragment offsets inside a buffer (the buffer index is static after the
+    // unroll by two, so it folds into the instructions' offset field)
+    uint32_t offa[TM][4], offb[TN][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
+            offa[i][s] = (uint32_t)lds_chunk(wm * WTM + i * 16 + lr, 4 * s + kg);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                tmp[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j)
+            offb[j][s] = (uint32_t)lds_chunk(wn * WTN + j * 16 + lr, 4 * s + kg);
+    }
+
+    for (int64_t g0 = 0; g0 < nk; g0 += 2) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            v8h fa[TM], fb[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 16 + lr;
-                fa[i] = *reinterpret_cast<const v8h*>(&lds_a[buf][lds_chunk(row, 4 * s + kg)]);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = wn * WTN + j * 16 + lr;
-                fb[j] = *reinterpret_cast<const v8h*>(&lds_b[buf][lds_chunk(col, 4 * s + kg)]);
-            }
+        for (int buf = 0; buf < 2; ++buf) {
+            const int64_t g = g0 + buf;
+            if (g >= nk)
+                break;                              // uniform: odd group count
+            v4f tmp[TM][TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], tmp[i][j], 0, 0, 0);
-            // (the group after the last re-stages the last one into the idle buffer)
-            if (s == 0)
-                store_a(buf ^ 1);
-            if (s == 1) {
-                store_b(buf ^ 1);
-                load_global(g + 2 < nk ? g + 2 : nk - 1);
-            }
-        }
-
-        // Promotion with this group's scale products.
-        float sbs = 0.f;
-        if constexpr (MODE == Mode::Fwd)
-            sbs = p.sb[(n0 / kGroup) * G + g];
-        else if constexpr (MODE == Mode::Dgrad)
-            sbs = p.sb[g * (p.N / kGroup) + n0 / kGroup];
+                    tmp[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const v4f sav = *reinterpret_cast<const v4f*>(&lds_sa[buf][wm * WTM + i * 16 + 4 * kg]);
-            if constexpr (MODE == Mode::Wgrad) {
+            for (int s = 0; s < 4; ++s) {
+                v8h fa[TM], fb[TN];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const float sbc = lds_sb[buf][wn * WTN + j * 16 + lr];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[i][j][v] = fmaf(tmp[i][j][v], sav[v] * sbc, acc[i][j][v]);
-                }
-            } else {
-                float ps[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    ps[v] = sav[v] * sbs;
+                for (int i = 0; i < TM; ++i)
+                    fa[i] = *reinterpret_cast<const v8h*>(&lds_a[buf][offa[i][s]]);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
+                    fb[j] = *reinterpret_cast<const v8h*>(&lds_b[buf][offb[j][s]]);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[i][j][v] = fmaf(tmp[i][j][v], ps[v], acc[i][j][v]);
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], tmp[i][j], 0, 0, 0);
+                // (the group after the last re-stages the last one into the idle buffer)
+                if (s == 0)
+                    store_a(buf ^ 1);
+                if (s == 1) {
+                    store_b(buf ^ 1);
+                    load_global(g + 2 < nk ? g + 2 : nk - 1);
+                }
             }
-        }
 
-        __syncthreads();
+            // Promotion with this group's scale products.
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const v4f sav = *reinterpret_cast<const v4f*>(&lds_sa[buf][wm * WTM + i * 16 + 4 * kg]);
+                if constexpr (MODE == Mode::Wgrad) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const float sbc = lds_sb[buf][wn * WTN + j * 16 + lr];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[i][j][v] = fmaf(tmp[i][j][v], sav[v] * sbc, acc[i][j][v]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[i][j][v] = fmaf(tmp[i][j][v], sav[v], acc[i][j][v]);
+                }
+            }
+
+            __syncthreads();
+        }
     }
 
     // ------------------------------------------------ epilogue
