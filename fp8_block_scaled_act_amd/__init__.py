@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose",
-    "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
+    "fp8_gemm_fwd", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -46,6 +46,7 @@ _SYMBOLS = {
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p], ctypes.c_int),
     "fp8_gemm_fwd": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8_linear_fwd": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 4, ctypes.c_int),
     "fp8_gemm_dgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_gemm_wgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
@@ -190,6 +191,27 @@ def fp8_gemm_fwd(xq, sx, wq, sw, out=None, stream=None):
     _check(lib().fp8_gemm_fwd(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
            "fp8_gemm_fwd")
     return y
+
+
+def fp8_linear_fwd(x, wq, sw, out=None, stream=None):
+    """Quantize x bf16 [M,K] (1x128) and multiply by the quantized W [N,K]:
+    returns (y bf16 [M,N], xq u8 [M,K], sx f32 [M,K/128])."""
+    M, K = x.shape
+    N = wq.shape[0]
+    _expect(x, "x", torch.bfloat16, (M, K))
+    _expect(wq, "wq", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    if out is None:
+        y, q, s = (_empty((M, N), torch.bfloat16, x), _empty((M, K), torch.uint8, x),
+                   _empty((M, K // GROUP), torch.float32, x))
+    else:
+        y, q, s = out
+    _expect(y, "y", torch.bfloat16, (M, N))
+    _expect(q, "xq", torch.uint8, (M, K))
+    _expect(s, "sx", torch.float32, (M, K // GROUP))
+    _check(lib().fp8_linear_fwd(_ptr(x), _ptr(wq), _ptr(sw), M, N, K, _ptr(q), _ptr(s), _ptr(y), _stream(stream)),
+           "fp8_linear_fwd")
+    return y, q, s
 
 
 def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):

@@ -290,6 +290,41 @@ fp8lin_status fp8_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq
     return end_launch();
 }
 
+fp8lin_status fp8_linear_fwd(const void* x, const uint8_t* wq, const float* sw, int64_t M, int64_t N, int64_t K,
+                             uint8_t* xq, float* sx, void* y, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || N % kGroup != 0 || K % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bx, bq, bsx, bw, bsw, by;
+    if (!bytes_of(M, K, 2, &bx) || !bytes_of(M, K, 1, &bq) || !bytes_of(M, K / kGroup, 4, &bsx) ||
+        !bytes_of(N, K, 1, &bw) || !bytes_of(N / kGroup, K / kGroup, 4, &bsw) || !bytes_of(M, N, 2, &by))
+        return FP8LIN_ERR_SHAPE;
+    int64_t tm = (M + 127) / 128, tn = (N + 127) / 128, nb;
+    if (!mul_ok(tm, tn, &nb) || nb > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    if (by == 0)
+        bw = bsw = 0;
+    const Buf in[] = {{x, bx}, {wq, bw}, {sw, bsw}};
+    const Buf out[] = {{xq, bq}, {sx, bsx}, {y, by}};
+    fp8lin_status s = check_buffers(in, 3, out, 3);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bq == 0 && by == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    const hipStream_t st = as_stream(stream);
+    if (bq > 0)
+        fp8lin::launch_quant_rowgroup(x, M * (K / kGroup), xq, sx, st);
+    if (by > 0) {
+        if (K == 0)
+            fp8lin::launch_fill_zero_bf16(y, M * N, st);
+        else
+            fp8lin::launch_gemm_fwd(xq, sx, wq, sw, M, N, K, y, st);
+    }
+    return end_launch();
+}
+
 fp8lin_status fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t T,
                              int64_t N, int64_t K, void* dx, void* stream)
 {

@@ -158,6 +158,26 @@ fp8lin_status fp8_gemm_fwd(const uint8_t* xq, const float* sx,
                            void* y, void* stream);
 
 /*
+ * One forward / rollout linear step from BF16 activations, in one call:
+ *   fp8_quant_act(x) -> (xq, sx), then y = fp8_gemm_fwd(xq, sx, wq, sw),
+ * enqueued as those two kernels on the stream.
+ * Jet-RL summary, "Quantization scheme" and "Core architecture": the
+ * activation of a linear layer is quantized 1x128 right before its FP8 GEMM,
+ * the same way for rollout and training; xq / sx are also the FP8 copy of the
+ * activation that the backward pass keeps.
+ *   x    : BF16 [M,K]                              (input)
+ *   wq   : uint8 [N,K], sw : float [N/128][K/128]  (input, fp8_quant_weight)
+ *   xq   : uint8 [M,K], sx : float [M][K/128]      (output)
+ *   y    : BF16 [M,N]                              (output)
+ * Outputs are bit-identical to the two separate calls.
+ * N % 128 == 0 and K % 128 == 0; M >= 0 is free.  M == 0 is an OK no-op;
+ * N == 0 only quantizes; K == 0 writes zeros to y.
+ */
+fp8lin_status fp8_linear_fwd(const void* x, const uint8_t* wq, const float* sw,
+                             int64_t M, int64_t N, int64_t K,
+                             uint8_t* xq, float* sx, void* y, void* stream);
+
+/*
  * DGrad GEMM (NN):  dX = dY W, contracted over W's row dimension N.
  * Jet-RL summary, "Quantization scheme": the backward DGrad GEMM runs in FP8.
  *   dX[t,k] = sum_g sdy[t][g] * sw[g][k/128] * sum_{n in g} dec(dyq[t,n]) dec(wq[n,k])

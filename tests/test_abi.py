@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert len(names) >= 11, names
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
-              "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -124,6 +124,25 @@ def test_gemm_validation(L):
     assert L.fp8_gemm_wgrad(A, B, C, D, 5, 7, 100, E, s0) == SHAPE                 # T % 128
     assert L.fp8_gemm_wgrad(A, B, C, D, 5, 7, 128, A, s0) == ALIAS
     assert L.fp8_gemm_wgrad(None, None, None, None, 5, 0, 128, None, s0) == OK
+
+
+@fake_ptrs
+def test_linear_fwd_validation(L):
+    # x, wq, sw, M, N, K, xq, sx, y
+    assert L.fp8_linear_fwd(A, B, C, 4, 100, 128, D, E, F, s0) == SHAPE
+    assert L.fp8_linear_fwd(A, B, C, 4, 128, 100, D, E, F, s0) == SHAPE
+    assert L.fp8_linear_fwd(A, B, C, -1, 128, 128, D, E, F, s0) == SHAPE
+    assert L.fp8_linear_fwd(A, None, C, 4, 128, 128, D, E, F, s0) == NULL
+    assert L.fp8_linear_fwd(A, B, C, 4, 128, 128, None, E, F, s0) == NULL
+    assert L.fp8_linear_fwd(A, B, C, 4, 128, 128, D, E, F + 8, s0) == ALIGN
+    assert L.fp8_linear_fwd(A, B, C, 4, 128, 128, A + 256, E, F, s0) == ALIAS   # xq over x
+    assert L.fp8_linear_fwd(A, B, C, 4, 128, 128, D, E, B, s0) == ALIAS         # y over wq
+    assert L.fp8_linear_fwd(A, B, C, 4, 128, 128, D, D + 256, F, s0) == ALIAS   # sx over xq
+    assert L.fp8_linear_fwd(None, None, None, 0, 128, 128, None, None, None, s0) == OK
+    # N == 0 still quantizes x, so the weights may be NULL but x may not
+    assert L.fp8_linear_fwd(None, None, None, 4, 0, 128, D, E, None, s0) == NULL
+    assert L.fp8_linear_fwd(A, None, None, 4, 0, 128, D, E, None, s0) == DEVICE
+    assert L.fp8_linear_fwd(A, B, C, 4, 128, 128, D, E, F, s0) == DEVICE
 
 
 @fake_ptrs
