@@ -636,6 +636,14 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* g)
                  "v"(g)
                  : "memory");
 }
+// The 4-byte form: lane l's word lands at M0 + 4 * l.
+__device__ __forceinline__ void dma4(uint32_t lds, const void* g)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(
+                     __builtin_amdgcn_readfirstlane(lds)),
+                 "v"(g)
+                 : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vm()
 {
@@ -825,6 +833,219 @@ __global__ __launch_bounds__(640) void gemm_fwd_decode_kernel(const GemmArgs p)
     }
 }
 
+// ------------------------------------------------------------ large NT GEMM
+//
+// C[m][n] = sum_g sa(m, g) sb(n, g) sum_{k in g} dec(a[m][k]) dec(b[n][k]) for
+// the forward GEMM (sb(n, g) = sb[n / 128][g], a 128x128 weight block) and
+// WGrad (sb(n, g) = sb[n][g]); both operands are row-major with the
+// contraction contiguous.  One workgroup of eight waves computes a 256 x 128
+// tile of C, one 128-wide group per step:
+//  * every wave streams its share of the step's operands straight from
+//    global memory into LDS with global_load_lds (7 instructions per wave and
+//    step: 4 x 1 KB of A codes, 2 x 1 KB of B codes, one 256-byte run of row
+//    scales), three steps deep; one barrier per step publishes step g and
+//    retires step g - 1, whose slot then receives step g + 2;
+//  * wave w multiplies A rows [64 (w % 4), +64) by B rows [64 (w / 4), +64)
+//    as 2 x 2 tiles of v_mfma_f32_32x32x16_f16, converting codes exactly to
+//    fp16 after the LDS read (v_cvt_scalef32_pk_f16_fp8, scale 1), and adds
+//    each step's fp32 partial sums into the accumulators times sa * sb.
+// MFMA side: B rows are the instruction's M side and A rows its N side, so a
+// lane's 16 results share one A row (one sa per tile and step).  Lane (m, kh)
+// of k-step st of a step holds k in [32 (st / 2) + 16 kh + 8 (st % 2), +8)
+// for both operands, a fixed permutation of the group.
+// LDS: a row of a step is 128 bytes, its 16-byte piece q at position
+// q ^ ((row / 2) % 8), so the 16 rows a 16-lane fragment read touches cover
+// all banks; the DMA writes eight whole rows per instruction.
+namespace nt {
+constexpr int BA = 256, BB = 128;                  // A rows, B rows per tile
+constexpr int D = 3;                               // steps in flight
+constexpr int OFF_B = BA * kGroup;                 // 32768
+constexpr int OFF_SA = OFF_B + BB * kGroup;        // 49152
+constexpr int OFF_SB = OFF_SA + BA * 4;            // 50176
+constexpr int STAGE = 51200;                       // OFF_SB + BB * 4 = 50688, rounded to 1 KB
+constexpr int NDMA = 7;                            // DMA instructions per wave and step
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int piece(int row, int q) { return row * kGroup + ((q ^ ((row >> 1) & 7)) << 4); }
+
+struct Sources {
+    const uint8_t* a[4];                           // four 8-row runs of A codes
+    const uint8_t* b[2];                           // two 8-row runs of B codes
+    const float* s;                                // a 64-row run of A or B scales
+    uint32_t dst_s;                                // its LDS offset within a step
+};
+
+// One wave's share of step g into LDS slot `st` (an LDS byte address).
+__device__ __forceinline__ void issue_step(const Sources& src, int wave, uint32_t st, int64_t g)
+{
+    using namespace dec;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(st + (4 * wave + i) * 1024, src.a[i] + g * kGroup);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        dma16(st + OFF_B + (2 * wave + j) * 1024, src.b[j] + g * kGroup);
+    dma4(st + src.dst_s, src.s + g);
+}
+}  // namespace nt
+
+template <Mode MODE>
+__global__ __launch_bounds__(512) void gemm_nt_kernel(const GemmArgs p)
+{
+    using namespace dec;
+    using namespace nt;
+    static_assert(MODE == Mode::Fwd || MODE == Mode::Wgrad, "NT operands only");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[D * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t G = p.Kc / kGroup;
+    int tm, tn;
+    tile_coords((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BA, n0 = (int64_t)tn * BB;
+
+    // this wave's DMA sources (rows past the end read the last row; their
+    // results are never stored)
+    Sources src;
+    {
+        const int r8 = lane >> 3, pos = lane & 7;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 8 * (4 * wave + i) + r8;
+            const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
+            src.a[i] = p.a + gr * p.Kc + 16 * (pos ^ ((row >> 1) & 7));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 8 * (2 * wave + j) + r8;
+            const int64_t gr = n0 + row < p.N ? n0 + row : p.N - 1;
+            src.b[j] = p.b + gr * p.Kc + 16 * (pos ^ ((row >> 1) & 7));
+        }
+        if (wave < 4) {
+            const int64_t gr = m0 + 64 * wave + lane < p.M ? m0 + 64 * wave + lane : p.M - 1;
+            src.s = p.sa + gr * G;
+            src.dst_s = OFF_SA + 256 * wave;
+        } else {
+            // waves 6 and 7 repeat the B-scale runs of waves 4 and 5 (same
+            // values to the same words), so that every wave issues NDMA
+            const int64_t r = n0 + 64 * (wave & 1) + lane;
+            const int64_t gr = r < p.N ? r : p.N - 1;
+            src.s = MODE == Mode::Fwd ? p.sb + (gr / kGroup) * G : p.sb + gr * G;
+            src.dst_s = OFF_SB + 256 * (wave & 1);
+        }
+    }
+    const uint32_t base = (uint32_t)(uintptr_t)&lds[0];
+
+    const int wa = wave & 3, wb = wave >> 2;
+    const int m = lane & 31, kh = lane >> 5;
+    v16f acc[2][2];
+#pragma unroll
+    for (int at = 0; at < 2; ++at)
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[at][bt][r] = 0.f;
+
+#pragma unroll
+    for (int s0 = 0; s0 < D - 1; ++s0)
+        if (s0 < G)
+            issue_step(src, wave, base + s0 * STAGE, s0);
+    for (int64_t g = 0; g < G; ++g) {
+        if (g + 1 < G)
+            wait_vm<NDMA>();                       // step g landed (this wave's part)
+        else
+            wait_vm<0>();
+        __syncthreads();                           // all of step g landed; step g - 1 retired
+        if (g + D - 1 < G)
+            issue_step(src, wave, base + (uint32_t)(((g + D - 1) % D) * STAGE), g + D - 1);
+        const uint8_t* st = lds + (g % D) * STAGE;
+        v16f tmp[2][2];
+#pragma unroll
+        for (int at = 0; at < 2; ++at)
+#pragma unroll
+            for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    tmp[at][bt][r] = 0.f;
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp) {
+            const int q = 2 * kp + kh;
+            u32x4 av[2], bv[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                av[t] = *reinterpret_cast<const u32x4*>(st + piece(64 * wa + 32 * t + m, q));
+                bv[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(64 * wb + 32 * t + m, q));
+            }
+            v8h alo[2], ahi[2], blo[2], bhi[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                alo[t] = cvt8(av[t].x, av[t].y);
+                ahi[t] = cvt8(av[t].z, av[t].w);
+                blo[t] = cvt8(bv[t].x, bv[t].y);
+                bhi[t] = cvt8(bv[t].z, bv[t].w);
+            }
+#pragma unroll
+            for (int at = 0; at < 2; ++at)
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt) {
+                    tmp[at][bt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(blo[bt], alo[at], tmp[at][bt], 0, 0, 0);
+                    tmp[at][bt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bhi[bt], ahi[at], tmp[at][bt], 0, 0, 0);
+                }
+        }
+        const float* ssa = reinterpret_cast<const float*>(st + OFF_SA);
+        const float* ssb = reinterpret_cast<const float*>(st + OFF_SB);
+#pragma unroll
+        for (int at = 0; at < 2; ++at) {
+            const float sa = ssa[64 * wa + 32 * at + m];
+#pragma unroll
+            for (int bt = 0; bt < 2; ++bt) {
+                if constexpr (MODE == Mode::Fwd) {
+                    // the tile's 128 B rows lie in one weight block
+                    const float s = sa * ssb[0];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[at][bt][r] = fmaf(tmp[at][bt][r], s, acc[at][bt][r]);
+                } else {
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const f32x4 sb4 =
+                            *reinterpret_cast<const f32x4*>(ssb + 64 * wb + 32 * bt + 8 * a4 + 4 * kh);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[at][bt][4 * a4 + e] = fmaf(tmp[at][bt][4 * a4 + e], sa * sb4[e],
+                                                           acc[at][bt][4 * a4 + e]);
+                    }
+                }
+            }
+        }
+    }
+
+    // C rows are A rows (lane m of each tile), columns B rows: four
+    // consecutive columns per lane and 8-byte stores (N % 4 == 0)
+#pragma unroll
+    for (int at = 0; at < 2; ++at) {
+        const int64_t row = m0 + 64 * wa + 32 * at + m;
+        if (row >= p.M)
+            continue;
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int64_t col = n0 + 64 * wb + 32 * bt + 8 * a4 + 4 * kh;
+                if (col < p.N) {
+                    const int r0 = 4 * a4;
+                    const uint32_t v0 = (uint32_t)f32_to_bf16_rne(acc[at][bt][r0]) |
+                                        ((uint32_t)f32_to_bf16_rne(acc[at][bt][r0 + 1]) << 16);
+                    const uint32_t v1 = (uint32_t)f32_to_bf16_rne(acc[at][bt][r0 + 2]) |
+                                        ((uint32_t)f32_to_bf16_rne(acc[at][bt][r0 + 3]) << 16);
+                    *reinterpret_cast<u32x2*>(p.c + row * p.N + col) = u32x2{v0, v1};
+                }
+            }
+    }
+}
+
 // Zeros for an empty contraction (C = 0).  A kernel rather than a memset so
 // the call stays capturable without memset nodes.
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ c, int64_t n)
@@ -854,6 +1075,18 @@ void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st)
     fill_zero_kernel<<<(unsigned)(b < 1 ? 1 : b), 256, 0, st>>>(static_cast<uint16_t*>(c), n);
 }
 
+#ifndef NT_MIN_ROWS
+#define NT_MIN_ROWS 128                            // fewer C rows: the 128 x 128 tile
+#endif
+template <Mode MODE>
+static void launch_gemm_nt(GemmArgs p, hipStream_t st)
+{
+    p.tiles_m = (int)((p.M + nt::BA - 1) / nt::BA);
+    p.tiles_n = (int)((p.N + nt::BB - 1) / nt::BB);
+    const unsigned nblocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+    gemm_nt_kernel<MODE><<<nblocks, 512, 0, st>>>(p);
+}
+
 void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
                      int64_t N, int64_t K, void* y, hipStream_t st)
 {
@@ -867,8 +1100,10 @@ void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, cons
         gemm_fwd_skinny_kernel<4, 1, 2><<<(unsigned)(N / 64), 1024, 0, st>>>(p);
     else if (M <= 64)
         launch_gemm<64, 64, 1, 4, Mode::Fwd>(p, st);
-    else
+    else if (M <= NT_MIN_ROWS)
         launch_gemm<128, 128, 2, 4, Mode::Fwd>(p, st);
+    else
+        launch_gemm_nt<Mode::Fwd>(p, st);
 }
 
 void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t T,
@@ -889,8 +1124,10 @@ void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xT
     GemmArgs p{dyTq, sdyT, xTq, sxT, static_cast<uint16_t*>(dw), N, K, T, 0, 0};
     if (N <= 64)
         launch_gemm<64, 64, 1, 4, Mode::Wgrad>(p, st);
-    else
+    else if (N <= NT_MIN_ROWS || K % 4 != 0)
         launch_gemm<128, 128, 4, 2, Mode::Wgrad>(p, st);
+    else
+        launch_gemm_nt<Mode::Wgrad>(p, st);
 }
 
 }  // namespace fp8lin
