@@ -969,14 +969,28 @@ __global__ __launch_bounds__(512) void gemm_nt_kernel(const GemmArgs p)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     tmp[at][bt][r] = 0.f;
+        // pieces of k pair kp + 1 are read while pair kp is multiplied
+        u32x4 avn[2], bvn[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            avn[t] = *reinterpret_cast<const u32x4*>(st + piece(64 * wa + 32 * t + m, kh));
+            bvn[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(64 * wb + 32 * t + m, kh));
+        }
 #pragma unroll
         for (int kp = 0; kp < 4; ++kp) {
-            const int q = 2 * kp + kh;
             u32x4 av[2], bv[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                av[t] = *reinterpret_cast<const u32x4*>(st + piece(64 * wa + 32 * t + m, q));
-                bv[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(64 * wb + 32 * t + m, q));
+                av[t] = avn[t];
+                bv[t] = bvn[t];
+            }
+            if (kp < 3) {
+                const int q = 2 * (kp + 1) + kh;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    avn[t] = *reinterpret_cast<const u32x4*>(st + piece(64 * wa + 32 * t + m, q));
+                    bvn[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(64 * wb + 32 * t + m, q));
+                }
             }
             v8h alo[2], ahi[2], blo[2], bhi[2];
 #pragma unroll
@@ -986,13 +1000,18 @@ __global__ __launch_bounds__(512) void gemm_nt_kernel(const GemmArgs p)
                 blo[t] = cvt8(bv[t].x, bv[t].y);
                 bhi[t] = cvt8(bv[t].z, bv[t].w);
             }
+            // the four tiles' first k steps, then their second (a dependent
+            // pair is three instructions apart)
 #pragma unroll
             for (int at = 0; at < 2; ++at)
 #pragma unroll
-                for (int bt = 0; bt < 2; ++bt) {
+                for (int bt = 0; bt < 2; ++bt)
                     tmp[at][bt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(blo[bt], alo[at], tmp[at][bt], 0, 0, 0);
+#pragma unroll
+            for (int at = 0; at < 2; ++at)
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt)
                     tmp[at][bt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bhi[bt], ahi[at], tmp[at][bt], 0, 0, 0);
-                }
         }
         const float* ssa = reinterpret_cast<const float*>(st + OFF_SA);
         const float* ssb = reinterpret_cast<const float*>(st + OFF_SB);
