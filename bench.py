@@ -12,7 +12,9 @@ inputs already resident in HBM:
   prefill  7B-shaped forward: quantize X [8192,3584] and W [18944,3584], GEMM
   large    32B-shaped forward: quantize X [16384,5120] and W [27648,5120], GEMM
   backward 8B-shaped backward: dual transpose-quant of dY [8192,14336],
-           transpose-requant of the saved FP8 X [8192,4096], DGrad and WGrad
+           transpose-requant of the saved FP8 X [8192,4096], DGrad (as the NT
+           GEMM on the transposed FP8 weight, made once with the weight
+           quantization) and WGrad
   tiny     X [128,1024], W [1024,1024] (correctness-sized)
 The step is captured once in a HIP graph and replayed; K steps are timed
 between device synchronisations.  value = GEMM TFLOP/s of the whole step.
@@ -134,6 +136,7 @@ def build_step(name, torch, fl, synthetic):
         x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
         w = bf16(synthetic.weights(N, K, seed=0))
         wq, sw = fl.fp8_quant_weight(w)              # forward's weight quantization
+        wqT, swT = fl.fp8_weight_transpose(wq, sw)    # its transposed copy, made alongside for DGrad
         xq, sx = fl.fp8_quant_act(x)                  # saved FP8 activations of the forward
         torch.cuda.synchronize()
         del w, x
@@ -146,11 +149,14 @@ def build_step(name, torch, fl, synthetic):
                T * N * 2 + 2 * T * N + (N * (T // G) + T * (N // G)) * 4)
         st.add("quant_transpose_fp8_X", lambda i: fl.fp8_quant_transpose(xq, sx, out=(xTq, sxT, None, None)),
                "hbm", T * K + T * (K // G) * 4 + T * K + K * (T // G) * 4)
-        st.add("gemm_dgrad", lambda i: fl.fp8_gemm_dgrad(dyq, sdy, wq, sw, out=dx), "mfma", 2 * T * N * K)
+        # DGrad dX = dY W as the NT GEMM against W^T (same sums as fp8_gemm_dgrad)
+        st.add("gemm_dgrad", lambda i: fl.fp8_gemm_fwd(dyq, sdy, wqT, swT, out=dx), "mfma", 2 * T * N * K)
         st.add("gemm_wgrad", lambda i: fl.fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT, out=dw), "mfma", 2 * T * N * K)
         st.gemm_flop = 4 * T * N * K
         st.dominant = None
-        st.config = {"workload": wl.doc, "T": T, "N": N, "K": K, "outlier_columns": wl.n_out}
+        st.config = {"workload": wl.doc, "T": T, "N": N, "K": K, "outlier_columns": wl.n_out,
+                     "dgrad_weight": "transposed FP8 copy (fp8_weight_transpose), made with the weight "
+                                     "quantization outside the step"}
     return st
 
 
@@ -252,7 +258,7 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "quant_transpose_dual_dY": "quant_transpose_bf16_kernel",
     "quant_transpose_fp8_X": "quant_transpose_fp8_kernel",
     "gemm_fwd": "gemm_",
-    "gemm_dgrad": "Mode)1",
+    "gemm_dgrad": "Mode)0",     # the backward step runs DGrad as the NT GEMM on W^T
     "gemm_wgrad": "Mode)2",
 }
 

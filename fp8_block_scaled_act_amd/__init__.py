@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "lib", "Fp8LinError", "GROUP",
-    "fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose",
+    "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_quant_transpose",
     "fp8_gemm_fwd", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
@@ -42,6 +42,8 @@ _SYMBOLS = {
                        ctypes.c_void_p], ctypes.c_int),
     "fp8_quant_weight": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                           ctypes.c_void_p], ctypes.c_int),
+    "fp8_weight_transpose": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                              ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "fp8_quant_transpose": ([ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p], ctypes.c_int),
@@ -141,6 +143,21 @@ def fp8_quant_weight(w: torch.Tensor, out=None, stream=None):
     _expect(s, "sw", torch.float32, (N // GROUP, K // GROUP))
     _check(lib().fp8_quant_weight(_ptr(w), N, K, _ptr(q), _ptr(s), _stream(stream)), "fp8_quant_weight")
     return q, s
+
+
+def fp8_weight_transpose(wq: torch.Tensor, sw: torch.Tensor, out=None, stream=None):
+    """Exact transposed copy of a quantized weight: (wq u8 [N,K], sw f32 [N/128,K/128]) ->
+    (wqT u8 [K,N], swT f32 [K/128,N/128]).  DGrad is then fp8_gemm_fwd(dyq, sdy, wqT, swT)."""
+    N, K = wq.shape
+    _expect(wq, "wq", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    qT, sT = out if out is not None else (_empty((K, N), torch.uint8, wq),
+                                          _empty((K // GROUP, N // GROUP), torch.float32, wq))
+    _expect(qT, "wqT", torch.uint8, (K, N))
+    _expect(sT, "swT", torch.float32, (K // GROUP, N // GROUP))
+    _check(lib().fp8_weight_transpose(_ptr(wq), _ptr(sw), N, K, _ptr(qT), _ptr(sT), _stream(stream)),
+           "fp8_weight_transpose")
+    return qT, sT
 
 
 def fp8_quant_transpose(src: torch.Tensor, src_scales: torch.Tensor | None = None, dual: bool = False,

@@ -200,6 +200,29 @@ fp8lin_status fp8_quant_weight(const void* w, int64_t N, int64_t K, uint8_t* wq,
     return end_launch();
 }
 
+fp8lin_status fp8_weight_transpose(const uint8_t* wq, const float* sw, int64_t N, int64_t K, uint8_t* wqT,
+                                  float* swT, void* stream)
+{
+    if (N < 0 || K < 0 || N % kGroup != 0 || K % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    if (N / kGroup > kMaxGridY)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bq, bs;
+    if (!bytes_of(N, K, 1, &bq) || !bytes_of(N / kGroup, K / kGroup, 4, &bs))
+        return FP8LIN_ERR_SHAPE;
+    const Buf in[] = {{wq, bq}, {sw, bs}};
+    const Buf out[] = {{wqT, bq}, {swT, bs}};
+    fp8lin_status s = check_buffers(in, 2, out, 2);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bq == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_transpose_codes(wq, sw, N, K, wqT, swT, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_quant_transpose(int kind, const void* src, const float* src_scales, int64_t T, int64_t C,
                                   uint8_t* dstT, float* sT, uint8_t* dst_rowq, float* s_rowq, void* stream)
 {

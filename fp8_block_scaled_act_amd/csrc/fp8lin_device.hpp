@@ -232,4 +232,18 @@ __device__ __forceinline__ uint2 quantize8_bf16(uint4 v, const GroupScale& g)
     return make_uint2(e4m3_encode4(t[0], t[1], t[2], t[3]), e4m3_encode4(t[4], t[5], t[6], t[7]));
 }
 
+// 4x4 byte transpose: rows r0..r3 (4 bytes each) -> columns c0..c3.
+__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                             uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3)
+{
+    const uint32_t lo01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+    c0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    c1 = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    c2 = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    c3 = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
 }  // namespace fp8lin

@@ -13,6 +13,8 @@ void launch_quant_transpose_bf16(const void* x, int64_t T, int64_t C, uint8_t* q
                                  uint8_t* qrow, float* srow, hipStream_t st);
 void launch_quant_transpose_fp8(const uint8_t* src, const float* srow, int64_t T, int64_t C,
                                 uint8_t* qT, float* sT, hipStream_t st);
+void launch_transpose_codes(const uint8_t* src, const float* s, int64_t R, int64_t C, uint8_t* dst, float* sT,
+                            hipStream_t st);
 void launch_encode_probe(const float* in, int64_t n, uint8_t* out, int method, hipStream_t st);
 void launch_decode_probe(const uint8_t* in, int64_t n, float* out, int method, hipStream_t st);
 

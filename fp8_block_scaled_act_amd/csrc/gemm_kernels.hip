@@ -96,20 +96,6 @@ __device__ __forceinline__ void fp8x16_to_f16(u32x4 v, u32x4& lo, u32x4& hi)
     hi = u32x4{c.x, c.y, d.x, d.y};
 }
 
-// 4x4 byte transpose: rows r0..r3 (4 bytes each) -> columns c0..c3.
-__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
-                                             uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3)
-{
-    const uint32_t lo01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
-    const uint32_t lo23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-    c0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-    c1 = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-    c2 = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-    c3 = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
-}
-
 // Byte offset in an LDS row (256 bytes = 16 fp16 chunks) of logical chunk p.
 __device__ __forceinline__ int lds_chunk(int row, int p) { return row * 256 + ((p ^ swz(row)) << 4); }
 

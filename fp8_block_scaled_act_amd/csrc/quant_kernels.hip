@@ -152,6 +152,53 @@ __device__ __forceinline__ void store_code_tile(const uint8_t* ctile, uint8_t* _
     }
 }
 
+// ========================================================= weight transpose
+//
+// FP8 codes [R][C] -> [C][R] and 128x128 block scales [R/128][C/128] ->
+// [C/128][R/128], bit for bit (a 128x128 block is the same block either way).
+// One workgroup per 128x128 tile: rows are read 16 bytes per lane into an
+// LDS tile; each thread then gathers a 16-row x 4-column block as 4x4 byte
+// transposes and writes 4 output rows x 16 bytes (eight lanes cover one
+// 128-byte output row).
+__global__ __launch_bounds__(256) void transpose_codes_kernel(const uint8_t* __restrict__ src,
+                                                              const float* __restrict__ s, int64_t R,
+                                                              int64_t C, uint8_t* __restrict__ dst,
+                                                              float* __restrict__ sT)
+{
+    constexpr int kPitch = 33;                // dwords per LDS row (32 + 1 pad)
+    __shared__ uint32_t tile[128 * kPitch];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * kGroup;
+    const int64_t c0 = (int64_t)blockIdx.x * kGroup;
+    {
+        const int sub = tid & 7, row = tid >> 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = load_nt(src + (r0 + row + 32 * i) * C + c0 + sub * 16);
+            uint32_t* d = tile + (row + 32 * i) * kPitch + sub * 4;
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
+        }
+    }
+    if (tid == 0)
+        sT[(int64_t)blockIdx.x * gridDim.y + blockIdx.y] = s[(int64_t)blockIdx.y * gridDim.x + blockIdx.x];
+    __syncthreads();
+    const int rg = tid & 7;                   // source rows 16 rg .. 16 rg + 15
+    const int cq = tid >> 3;                  // source columns 4 cq .. 4 cq + 3
+    uint32_t out[4][4];                       // [column j][4-row block b]
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t* t = tile + (16 * rg + 4 * b) * kPitch + cq;
+        transpose4x4(t[0], t[kPitch], t[2 * kPitch], t[3 * kPitch], out[0][b], out[1][b], out[2][b], out[3][b]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(dst + (c0 + 4 * cq + j) * R + r0 + 16 * rg) =
+            make_uint4(out[j][0], out[j][1], out[j][2], out[j][3]);
+}
+
 // ==================================================== transpose, BF16 source
 //
 // Tile of 128 tokens (t) x 128 columns (c); one workgroup of 256 threads.
@@ -428,6 +475,13 @@ void launch_quant_block(const void* w, int64_t N, int64_t K, uint8_t* q, float* 
 {
     dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
     quant_block_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(w), K, q, s);
+}
+
+void launch_transpose_codes(const uint8_t* src, const float* s, int64_t R, int64_t C, uint8_t* dst, float* sT,
+                            hipStream_t st)
+{
+    dim3 grid((unsigned)(C / kGroup), (unsigned)(R / kGroup));
+    transpose_codes_kernel<<<grid, 256, 0, st>>>(src, s, R, C, dst, sT);
 }
 
 void launch_quant_transpose_bf16(const void* x, int64_t T, int64_t C, uint8_t* qT, float* sT,

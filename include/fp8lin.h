@@ -114,6 +114,24 @@ fp8lin_status fp8_quant_weight(const void* w, int64_t N, int64_t K,
                                uint8_t* wq, float* sw, void* stream);
 
 /*
+ * Transposed copy of a quantized weight, for DGrad (once per optimizer step,
+ * next to fp8_quant_weight).  Jet-RL summary, "Quantization scheme" (DGrad
+ * in FP8 on the 128x128-quantized weight) and "Implementation" (custom
+ * transposition kernels).  A 128x128 block has one scale whichever way it is
+ * read, so the copy is exact:
+ *   wq  : uint8 [N,K], sw : float [N/128][K/128]   (input, fp8_quant_weight)
+ *   wqT : uint8 [K,N], swT : float [K/128][N/128]  (output)
+ *   wqT[k][n] = wq[n][k], swT[j][i] = sw[i][j].
+ * With it, DGrad is the forward GEMM on the transposed weight:
+ *   fp8_gemm_fwd(dyq, sdy, wqT, swT, T, K, N, dx)
+ * computes the same sums as fp8_gemm_dgrad(dyq, sdy, wq, sw, T, N, K, dx)
+ * (up to fp32 summation order) with both operands contraction-contiguous.
+ * N % 128 == 0 and K % 128 == 0.  N == 0 or K == 0 is an OK no-op.
+ */
+fp8lin_status fp8_weight_transpose(const uint8_t* wq, const float* sw, int64_t N, int64_t K,
+                                   uint8_t* wqT, float* swT, void* stream);
+
+/*
  * Transpose-quantization along tokens, 128x1 groups (WGrad operands).
  * Jet-RL summary, "Quantization scheme" (WGrad uses 1x128 and 128x1
  * quantization) and "Implementation" (custom transposition kernels).

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert len(names) >= 11, names
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
-              "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_linear_fwd", "fp8_weight_transpose", "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -143,6 +143,18 @@ def test_linear_fwd_validation(L):
     assert L.fp8_linear_fwd(None, None, None, 4, 0, 128, D, E, None, s0) == NULL
     assert L.fp8_linear_fwd(A, None, None, 4, 0, 128, D, E, None, s0) == DEVICE
     assert L.fp8_linear_fwd(A, B, C, 4, 128, 128, D, E, F, s0) == DEVICE
+
+
+@fake_ptrs
+def test_weight_transpose_validation(L):
+    assert L.fp8_weight_transpose(A, B, 100, 128, C, D, s0) == SHAPE
+    assert L.fp8_weight_transpose(A, B, 128, 100, C, D, s0) == SHAPE
+    assert L.fp8_weight_transpose(A, B, 128 * 70000, 128, C, D, s0) == SHAPE   # grid limit
+    assert L.fp8_weight_transpose(A, None, 128, 128, C, D, s0) == NULL
+    assert L.fp8_weight_transpose(A, B, 128, 128, A, D, s0) == ALIAS
+    assert L.fp8_weight_transpose(A, B, 128, 128, C + 4, D, s0) == ALIGN
+    assert L.fp8_weight_transpose(None, None, 0, 128, None, None, s0) == OK
+    assert L.fp8_weight_transpose(A, B, 128, 128, C, D, s0) == DEVICE
 
 
 @fake_ptrs

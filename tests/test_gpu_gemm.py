@@ -185,6 +185,19 @@ def test_dgrad_permutation_exact():
     assert np.array_equal(dx, oracle.f64_to_bf16(oracle.gemm_dgrad(dyq, sdy, wq, sw)))
 
 
+@pytest.mark.parametrize("T,N,K", [(5, 128, 256), (200, 256, 384), (1000, 512, 256)])
+def test_dgrad_via_transposed_weight(T, N, K):
+    """DGrad as the forward GEMM on fp8_weight_transpose's copy of W: the same
+    sums as the oracle's DGrad (a6), and the copy itself is exactly W^T."""
+    dyq, sdy = codes_scales((T, N), (T, N // G), T + N, 25)
+    wq, sw = codes_scales((N, K), (N // G, K // G), N + K, 26)
+    say("weight transpose + fwd as dgrad", T, N, K)
+    wqT, swT = fl.fp8_weight_transpose(u8_to_dev(wq), f32_to_dev(sw))
+    assert np.array_equal(host(wqT), wq.T) and np.array_equal(host(swT), sw.T)
+    dx = fl.fp8_gemm_fwd(u8_to_dev(dyq), f32_to_dev(sdy), wqT, swT)
+    check_metric(host(dx), oracle.gemm_dgrad(dyq, sdy, wq, sw), "dgrad(wT) %dx%dx%d" % (T, N, K))
+
+
 # -------------------------------------------------------------------- WGrad
 
 @pytest.mark.parametrize("N,K,T", [(1, 1, 128), (5, 77, 256), (64, 128, 128), (130, 200, 384),
@@ -275,11 +288,17 @@ def test_backward_full_size_sampled():
     xTq, sxT = fl.fp8_quant_transpose(xq, sx)
     say("backward full: dgrad")
     dx = fl.fp8_gemm_dgrad(dyq, sdy, wq, sw)
+    say("backward full: dgrad on the transposed weight")
+    wqT, swT = fl.fp8_weight_transpose(wq, sw)
+    dx_t = fl.fp8_gemm_fwd(dyq, sdy, wqT, swT)
+    del wqT, swT
     say("backward full: wgrad")
     dw = fl.fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT)
     rows_t = sampled_rows(T, seed=1)
     rows_n = sampled_rows(N, seed=2)
     dxg = host(dx[torch.from_numpy(rows_t).to(DEV)])
+    dxg_t = host(dx_t[torch.from_numpy(rows_t).to(DEV)])
+    del dx_t
     dwg = host(dw[torch.from_numpy(rows_n).to(DEV)])
     del dx, dw, wq, sw, xq, sx, dyTq, sdyT, dyq, sdy, xTq, sxT
     torch.cuda.empty_cache()
@@ -287,6 +306,7 @@ def test_backward_full_size_sampled():
     dyq_o, sdy_o = oracle.quant_act(dy[rows_t])
     ref_dx = oracle.gemm(oracle.dequant_rowgroup(dyq_o, sdy_o), oracle.dequant_block(owq, osw), b_trans=True)
     check_metric(dxg, ref_dx, "dgrad full")
+    check_metric(dxg_t, ref_dx, "dgrad full (transposed weight)")
     dyTq_o, sdyT_o = oracle.quant_act(np.ascontiguousarray(dy[:, rows_n].T))
     oxq, osx = oracle.quant_act(x)
     xTq_o, sxT_o = oracle.quant_transpose_fp8(oxq, osx)

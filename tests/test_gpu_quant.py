@@ -227,6 +227,19 @@ def test_quant_weight_full_size(name, N, K):
 
 # ------------------------------------------------- transpose along tokens
 
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 384), (14336, 4096)])
+def test_weight_transpose(N, K):
+    """fp8_weight_transpose of the GPU weight quantization equals the oracle's
+    codes and block scales, transposed, bit for bit."""
+    w = synthetic.weights(N, K, seed=N + K)
+    say("weight transpose", N, K)
+    wq, sw = fl.fp8_quant_weight(bf16_to_dev(w))
+    wqT, swT = fl.fp8_weight_transpose(wq, sw)
+    oq, osc = oracle.quant_weight(w)
+    assert np.array_equal(host(wqT), np.ascontiguousarray(oq.T))
+    assert np.array_equal(host(swT).view(np.uint32), np.ascontiguousarray(osc.T).view(np.uint32))
+
+
 @pytest.mark.parametrize("T,C", [(128, 1), (128, 77), (256, 200), (384, 256), (128, 1000)])
 def test_quant_transpose_bf16_small(T, C):
     x = synthetic.activations(T, C, seed=T + C, n_out=1)
