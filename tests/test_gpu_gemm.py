@@ -38,6 +38,31 @@ def test_fwd_random_codes(M, N, K):
     check_metric(host(y), oracle.gemm_fwd(xq, sx, wq, sw), "fwd %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [(4359, 4096, 384), (4359, 4096, 128), (2048, 8192, 256)])
+def test_fwd_many_tiles_sampled(M, N, K):
+    """More 256x128 tiles than workgroups: each workgroup runs several tiles
+    back to back with its step ring crossing tile boundaries (K/128 >= 2),
+    or one tile each (K = 128); checked on sampled rows incl. the ragged tail."""
+    xq, sx = codes_scales((M, K), (M, K // G), M + K, 41)
+    wq, sw = codes_scales((N, K), (N // G, K // G), N + K, 42)
+    say("gemm_fwd many tiles", M, N, K)
+    y = fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw))
+    rows = sampled_rows(M, n=24, seed=3)
+    yg = host(y[torch.from_numpy(rows).to(DEV)])
+    check_metric(yg, oracle.gemm_fwd(xq[rows], sx[rows], wq, sw), "fwd many tiles %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("N,K,T", [(4500, 2048, 256), (4500, 2048, 384)])
+def test_wgrad_many_tiles_sampled(N, K, T):
+    dyTq, sdyT = codes_scales((N, T), (N, T // G), N + T, 43)
+    xTq, sxT = codes_scales((K, T), (K, T // G), K + T, 44)
+    say("gemm_wgrad many tiles", N, K, T)
+    dw = fl.fp8_gemm_wgrad(u8_to_dev(dyTq), f32_to_dev(sdyT), u8_to_dev(xTq), f32_to_dev(sxT))
+    rows = sampled_rows(N, n=24, seed=4)
+    dwg = host(dw[torch.from_numpy(rows).to(DEV)])
+    check_metric(dwg, oracle.gemm_wgrad(dyTq[rows], sdyT[rows], xTq, sxT), "wgrad many tiles")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 128, 512), (17, 256, 1024), (64, 384, 2048), (64, 128, 1536),
                                    (33, 128, 16384), (64, 256, 15872), (64, 512, 14336), (40, 128, 768),
                                    (64, 128, 256), (3, 256, 17408)])
