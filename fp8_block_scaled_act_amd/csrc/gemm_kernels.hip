@@ -824,14 +824,14 @@ __global__ __launch_bounds__(640) void gemm_fwd_decode_kernel(const GemmArgs p)
 // C[m][n] = sum_g sa(m, g) sb(n, g) sum_{k in g} dec(a[m][k]) dec(b[n][k]) for
 // the forward GEMM (sb(n, g) = sb[n / 128][g], a 128x128 weight block) and
 // WGrad (sb(n, g) = sb[n][g]); both operands are row-major with the
-// contraction contiguous.  One workgroup of eight waves computes a 256 x 128
-// tile of C, one 128-wide group per step:
+// contraction contiguous.  A workgroup of four waves computes a 128 x 128
+// tile of C, two workgroups per CU, one 128-wide group per step:
 //  * every wave streams its share of the step's operands straight from
-//    global memory into LDS with global_load_lds (7 instructions per wave and
-//    step: 4 x 1 KB of A codes, 2 x 1 KB of B codes, one 256-byte run of row
-//    scales), three steps deep; one barrier per step publishes step g and
-//    retires step g - 1, whose slot then receives step g + 2;
-//  * wave w multiplies A rows [64 (w % 4), +64) by B rows [64 (w / 4), +64)
+//    global memory into LDS with global_load_lds (9 instructions per wave and
+//    step: 4 x 1 KB of A codes, 4 x 1 KB of B codes, one 256-byte run of row
+//    scales), two steps deep; one barrier per step publishes step g and
+//    retires step g - 1, whose slot then receives step g + 1;
+//  * wave w multiplies A rows [64 (w % 2), +64) by B rows [64 (w / 2), +64)
 //    as 2 x 2 tiles of v_mfma_f32_32x32x16_f16, converting codes exactly to
 //    fp16 after the LDS read (v_cvt_scalef32_pk_f16_fp8, scale 1), and adds
 //    each step's fp32 partial sums into the accumulators times sa * sb.
@@ -843,45 +843,63 @@ __global__ __launch_bounds__(640) void gemm_fwd_decode_kernel(const GemmArgs p)
 // q ^ ((row / 2) % 8), so the 16 rows a 16-lane fragment read touches cover
 // all banks; the DMA writes eight whole rows per instruction.
 namespace nt {
-constexpr int BA = 256, BB = 128;                  // A rows, B rows per tile
-constexpr int D = 3;                               // steps in flight
-constexpr int OFF_B = BA * kGroup;                 // 32768
-constexpr int OFF_SA = OFF_B + BB * kGroup;        // 49152
-constexpr int OFF_SB = OFF_SA + BA * 4;            // 50176
-constexpr int STAGE = 51200;                       // OFF_SB + BB * 4 = 50688, rounded to 1 KB
-constexpr int NDMA = 7;                            // DMA instructions per wave and step
+// Tile shapes: BA A rows x 128 B rows per workgroup of NW waves (WA x 2 wave
+// grid of 64 x 64 sub-tiles), D steps in flight.
+template <int BA_, int NW_, int D_>
+struct Cfg {
+    static constexpr int BA = BA_, BB = 128, NW = NW_, D = D_;
+    static constexpr int WA = BA / 64;             // waves along A (WA x 2 = NW)
+    static constexpr int OFF_B = BA * kGroup;
+    static constexpr int OFF_SA = OFF_B + BB * kGroup;
+    static constexpr int OFF_SB = OFF_SA + BA * 4;
+    static constexpr int STAGE = (OFF_SB + BB * 4 + 1023) / 1024 * 1024;
+    static constexpr int NA = BA / 8 / NW;         // 1 KB A-code runs per wave and step
+    static constexpr int NB = BB / 8 / NW;         // 1 KB B-code runs per wave and step
+    static constexpr int NDMA = NA + NB + 1;       // + one 64-row run of scales
+    static_assert(WA * 2 == NW && NA * NW * 8 == BA && NB * NW * 8 == BB, "tile / wave split");
+};
+// Two workgroups per CU (2 x 66 KB of LDS): while one waits at its step
+// barrier the other computes.  Measured 5-8% ahead of one 256 x 128
+// workgroup of 8 waves with three steps in flight (Cfg<256, 8, 3>), with
+// bit-identical results.
+using Pair = Cfg<128, 4, 2>;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int piece(int row, int q) { return row * kGroup + ((q ^ ((row >> 1) & 7)) << 4); }
 
+template <class C>
 struct Sources {
-    const uint8_t* a[4];                           // four 8-row runs of A codes
-    const uint8_t* b[2];                           // two 8-row runs of B codes
+    const uint8_t* a[C::NA];                       // 8-row runs of A codes
+    const uint8_t* b[C::NB];                       // 8-row runs of B codes
     const float* s;                                // a 64-row run of A or B scales
     uint32_t dst_s;                                // its LDS offset within a step
 };
 
 // One wave's share of step g into LDS slot `st` (an LDS byte address).
-__device__ __forceinline__ void issue_step(const Sources& src, int wave, uint32_t st, int64_t g)
+template <class C>
+__device__ __forceinline__ void issue_step(const Sources<C>& src, int wave, uint32_t st, int64_t g)
 {
     using namespace dec;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(st + (4 * wave + i) * 1024, src.a[i] + g * kGroup);
+    for (int i = 0; i < C::NA; ++i)
+        dma16(st + (C::NA * wave + i) * 1024, src.a[i] + g * kGroup);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        dma16(st + OFF_B + (2 * wave + j) * 1024, src.b[j] + g * kGroup);
+    for (int j = 0; j < C::NB; ++j)
+        dma16(st + C::OFF_B + (C::NB * wave + j) * 1024, src.b[j] + g * kGroup);
     dma4(st + src.dst_s, src.s + g);
 }
 }  // namespace nt
 
-template <Mode MODE>
-__global__ __launch_bounds__(512) void gemm_nt_kernel(const GemmArgs p)
+template <Mode MODE, class C>
+__global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_nt_kernel(
+    const GemmArgs p)
 {
     using namespace dec;
     using namespace nt;
     static_assert(MODE == Mode::Fwd || MODE == Mode::Wgrad, "NT operands only");
+    constexpr int BA = C::BA, BB = C::BB, D = C::D, STAGE = C::STAGE;
+    constexpr int OFF_B = C::OFF_B, OFF_SA = C::OFF_SA, OFF_SB = C::OFF_SB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[D * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -893,28 +911,29 @@ __global__ __launch_bounds__(512) void gemm_nt_kernel(const GemmArgs p)
 
     // this wave's DMA sources (rows past the end read the last row; their
     // results are never stored)
-    Sources src;
+    Sources<C> src;
     {
         const int r8 = lane >> 3, pos = lane & 7;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 8 * (4 * wave + i) + r8;
+        for (int i = 0; i < C::NA; ++i) {
+            const int row = 8 * (C::NA * wave + i) + r8;
             const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
             src.a[i] = p.a + gr * p.Kc + 16 * (pos ^ ((row >> 1) & 7));
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = 8 * (2 * wave + j) + r8;
+        for (int j = 0; j < C::NB; ++j) {
+            const int row = 8 * (C::NB * wave + j) + r8;
             const int64_t gr = n0 + row < p.N ? n0 + row : p.N - 1;
             src.b[j] = p.b + gr * p.Kc + 16 * (pos ^ ((row >> 1) & 7));
         }
-        if (wave < 4) {
+        if (wave < C::WA) {
             const int64_t gr = m0 + 64 * wave + lane < p.M ? m0 + 64 * wave + lane : p.M - 1;
             src.s = p.sa + gr * G;
             src.dst_s = OFF_SA + 256 * wave;
         } else {
-            // waves 6 and 7 repeat the B-scale runs of waves 4 and 5 (same
-            // values to the same words), so that every wave issues NDMA
+            // the two B-scale runs; with more waves than runs, the extra waves
+            // repeat them (same values to the same words), so that every wave
+            // issues NDMA
             const int64_t r = n0 + 64 * (wave & 1) + lane;
             const int64_t gr = r < p.N ? r : p.N - 1;
             src.s = MODE == Mode::Fwd ? p.sb + (gr / kGroup) * G : p.sb + gr * G;
@@ -923,7 +942,7 @@ __global__ __launch_bounds__(512) void gemm_nt_kernel(const GemmArgs p)
     }
     const uint32_t base = (uint32_t)(uintptr_t)&lds[0];
 
-    const int wa = wave & 3, wb = wave >> 2;
+    const int wa = wave % C::WA, wb = wave / C::WA;
     const int m = lane & 31, kh = lane >> 5;
     v16f acc[2][2];
 #pragma unroll
@@ -937,15 +956,15 @@ __global__ __launch_bounds__(512) void gemm_nt_kernel(const GemmArgs p)
 #pragma unroll
     for (int s0 = 0; s0 < D - 1; ++s0)
         if (s0 < G)
-            issue_step(src, wave, base + s0 * STAGE, s0);
+            issue_step<C>(src, wave, base + s0 * STAGE, s0);
     for (int64_t g = 0; g < G; ++g) {
         if (g + 1 < G)
-            wait_vm<NDMA>();                       // step g landed (this wave's part)
+            wait_vm<(D - 2) * C::NDMA>();          // step g landed (this wave's part)
         else
             wait_vm<0>();
         __syncthreads();                           // all of step g landed; step g - 1 retired
         if (g + D - 1 < G)
-            issue_step(src, wave, base + (uint32_t)(((g + D - 1) % D) * STAGE), g + D - 1);
+            issue_step<C>(src, wave, base + (uint32_t)(((g + D - 1) % D) * STAGE), g + D - 1);
         const uint8_t* st = lds + (g % D) * STAGE;
         v16f tmp[2][2];
 #pragma unroll
@@ -1080,16 +1099,13 @@ void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st)
     fill_zero_kernel<<<(unsigned)(b < 1 ? 1 : b), 256, 0, st>>>(static_cast<uint16_t*>(c), n);
 }
 
-#ifndef NT_MIN_ROWS
-#define NT_MIN_ROWS 128                            // fewer C rows: the 128 x 128 tile
-#endif
-template <Mode MODE>
+template <Mode MODE, class C = nt::Pair>
 static void launch_gemm_nt(GemmArgs p, hipStream_t st)
 {
-    p.tiles_m = (int)((p.M + nt::BA - 1) / nt::BA);
-    p.tiles_n = (int)((p.N + nt::BB - 1) / nt::BB);
+    p.tiles_m = (int)((p.M + C::BA - 1) / C::BA);
+    p.tiles_n = (int)((p.N + C::BB - 1) / C::BB);
     const unsigned nblocks = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
-    gemm_nt_kernel<MODE><<<nblocks, 512, 0, st>>>(p);
+    gemm_nt_kernel<MODE, C><<<nblocks, C::NW * 64, 0, st>>>(p);
 }
 
 void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
@@ -1105,8 +1121,6 @@ void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, cons
         gemm_fwd_skinny_kernel<4, 1, 2><<<(unsigned)(N / 64), 1024, 0, st>>>(p);
     else if (M <= 64)
         launch_gemm<64, 64, 1, 4, Mode::Fwd>(p, st);
-    else if (M <= NT_MIN_ROWS)
-        launch_gemm<128, 128, 2, 4, Mode::Fwd>(p, st);
     else
         launch_gemm_nt<Mode::Fwd>(p, st);
 }
@@ -1129,7 +1143,7 @@ void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xT
     GemmArgs p{dyTq, sdyT, xTq, sxT, static_cast<uint16_t*>(dw), N, K, T, 0, 0};
     if (N <= 64)
         launch_gemm<64, 64, 1, 4, Mode::Wgrad>(p, st);
-    else if (N <= NT_MIN_ROWS || K % 4 != 0)
+    else if (K % 4 != 0)
         launch_gemm<128, 128, 4, 2, Mode::Wgrad>(p, st);
     else
         launch_gemm_nt<Mode::Wgrad>(p, st);
