@@ -664,23 +664,37 @@ __device__ __forceinline__ void stream_operand(const uint8_t* src, int64_t rows,
         rp[i] = src + (r < rows ? r : rows - 1) * Kc + 16 * (x ^ ((4 * i + lr4) & 15));
     }
     auto chunk = [&](int64_t c, int slot) {
-        const int64_t cc = c < nch ? c : nch - 1;  // past the end: a harmless re-read
         const uint32_t dst = base + (uint32_t)(slot * WCH);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            dma16(dst + i * 1024, rp[i] + cc * (CH * kGroup));
+            dma16(dst + i * 1024, rp[i] + c * (CH * kGroup));
     };
+    // waits until chunk c has landed when the chunks after it up to c + D - 2
+    // (those that exist) were issued after it (vmcnt retires in order)
+    auto wait_chunk = [&](int64_t c) {
+        const int64_t after = nch - 1 - c < D - 2 ? nch - 1 - c : D - 2;
+        if (after >= 2)
+            wait_vm<32>();
+        else if (after == 1)
+            wait_vm<16>();
+        else
+            wait_vm<0>();
+    };
+    static_assert(D - 2 <= 2, "wait_chunk covers up to two chunks in flight behind the awaited one");
 #pragma unroll
     for (int c = 0; c < D - 1; ++c)
-        chunk(c, c);
-    wait_vm<(D - 2) * 16>();                       // chunk 0 landed
+        if (c < nch)
+            chunk(c, c);
+    wait_chunk(0);                                 // chunk 0 landed
     __syncthreads();
     for (int64_t c = 0; c < nch; ++c) {
-        chunk(c + D - 1, (int)((c + D - 1) % D));  // into the slot drained before the last barrier
-        wait_vm<(D - 2) * 16>();                   // chunk c + 1 landed
+        if (c + D - 1 < nch)
+            chunk(c + D - 1, (int)((c + D - 1) % D));  // into the slot drained before the last barrier
+        if (c + 1 < nch)
+            wait_chunk(c + 1);                     // chunk c + 1 landed
         __syncthreads();
     }
-    wait_vm<0>();                                  // no DMA may outlive the loop
+    wait_vm<0>();                                  // nothing is in flight any more
     __syncthreads();
     __syncthreads();
 }
