@@ -182,6 +182,28 @@ def test_fwd_rows_independent_of_batch():
     assert oracle.gemm_metric(bf16_bits_to_f64(y_64), bf16_bits_to_f64(y_all[128:192])) <= TOL
 
 
+@pytest.mark.parametrize("kind,M,N,K", [("fwd", 64, 14336, 4096), ("fwd", 300, 1024, 1024),
+                                        ("dgrad", 300, 1024, 512), ("wgrad", 512, 384, 1024)])
+def test_gemm_deterministic(kind, M, N, K):
+    """No atomics and a fixed summation order: repeated calls give the same
+    bits (decode streaming kernel, NT tiles, DGrad and WGrad paths)."""
+    a, sa = codes_scales((M, K), (M, K // G), M + N + K, 51)
+    if kind == "fwd":
+        b, sb = codes_scales((N, K), (N // G, K // G), N + K, 52)
+        fn = fl.fp8_gemm_fwd
+    elif kind == "dgrad":                       # dY [T=M, N=K here], W [K, N]
+        b, sb = codes_scales((K, N), (K // G, N // G), N + K, 53)
+        fn = fl.fp8_gemm_dgrad
+    else:                                       # dY^T [M, T=K], X^T [N, T=K]
+        b, sb = codes_scales((N, K), (N, K // G), N + K, 54)
+        fn = fl.fp8_gemm_wgrad
+    args = [u8_to_dev(a), f32_to_dev(sa), u8_to_dev(b), f32_to_dev(sb)]
+    say("gemm determinism", kind, M, N, K)
+    first = host(fn(*args))
+    for _ in range(3):
+        assert np.array_equal(host(fn(*args)), first)
+
+
 # -------------------------------------------------------------------- DGrad
 
 @pytest.mark.parametrize("T,N,K", [(1, 128, 128), (7, 256, 128), (64, 384, 256), (129, 256, 384),
