@@ -16,13 +16,20 @@
 // 448.03125; errors reach 2^-11.6 of the largest product on random codes).
 // With the outlier channels of real activations that error exceeds the
 // layer's accuracy bound.  Every E4M3 value is exactly an fp16 value, so the
-// codes are converted exactly to fp16 while they are staged into LDS
-// (v_cvt_scalef32_pk_f16_fp8, scale 1) and multiplied on the fp16 matrix
-// core (v_mfma_f32_16x16x32_f16, measured error <= 2^-20 of the largest
-// product).  HBM traffic stays one byte per operand element.
+// codes are converted exactly to fp16 (v_cvt_scalef32_pk_f16_fp8, scale 1)
+// and multiplied on the fp16 matrix core (measured error <= 2^-20 of the
+// largest product).  HBM traffic stays one byte per operand element.
 //
-// One workgroup: 256 threads = 4 waves on a WM x WN grid, tile BM x BN of C,
-// contraction stepped one group (128) at a time:
+// Kernels in this file:
+//   gemm_kernel            generic tile; DGrad on the untransposed weight and
+//                          a few small shapes (described below);
+//   gemm_fwd_skinny_kernel forward for <= 64 rows and very long K;
+//   gemm_fwd_decode_kernel forward for <= 64 rows: W streamed by LDS DMA;
+//   gemm_nt_kernel         forward, WGrad and DGrad on the transposed
+//                          weight: 128x128 tiles fed by LDS DMA.
+//
+// gemm_kernel: one workgroup of WM x WN waves, tile BM x BN of C, contraction
+// stepped one group (128) at a time:
 //   - FP8 operand tiles are read from global (16-byte loads), converted and
 //     written to LDS as fp16, double-buffered: group g+1 is in flight while
 //     group g is multiplied;
