@@ -149,8 +149,8 @@ def build_step(name, torch, fl, synthetic):
                T * N * 2 + 2 * T * N + (N * (T // G) + T * (N // G)) * 4)
         st.add("quant_transpose_fp8_X", lambda i: fl.fp8_quant_transpose(xq, sx, out=(xTq, sxT, None, None)),
                "hbm", T * K + T * (K // G) * 4 + T * K + K * (T // G) * 4)
-        # DGrad dX = dY W as the NT GEMM against W^T (same sums as fp8_gemm_dgrad)
-        st.add("gemm_dgrad", lambda i: fl.fp8_gemm_fwd(dyq, sdy, wqT, swT, out=dx), "mfma", 2 * T * N * K)
+        # DGrad dX = dY W on the transposed weight (same sums as fp8_gemm_dgrad)
+        st.add("gemm_dgrad", lambda i: fl.fp8_gemm_dgrad_t(dyq, sdy, wqT, swT, out=dx), "mfma", 2 * T * N * K)
         st.add("gemm_wgrad", lambda i: fl.fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT, out=dw), "mfma", 2 * T * N * K)
         st.gemm_flop = 4 * T * N * K
         st.dominant = None

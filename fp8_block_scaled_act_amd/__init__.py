@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_quant_transpose",
-    "fp8_gemm_fwd", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
+    "fp8_gemm_fwd", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -50,6 +50,7 @@ _SYMBOLS = {
     "fp8_gemm_fwd": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_linear_fwd": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 4, ctypes.c_int),
     "fp8_gemm_dgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8_gemm_dgrad_t": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_gemm_wgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
                            ctypes.c_int),
@@ -147,7 +148,7 @@ def fp8_quant_weight(w: torch.Tensor, out=None, stream=None):
 
 def fp8_weight_transpose(wq: torch.Tensor, sw: torch.Tensor, out=None, stream=None):
     """Exact transposed copy of a quantized weight: (wq u8 [N,K], sw f32 [N/128,K/128]) ->
-    (wqT u8 [K,N], swT f32 [K/128,N/128]).  DGrad is then fp8_gemm_fwd(dyq, sdy, wqT, swT)."""
+    (wqT u8 [K,N], swT f32 [K/128,N/128]), for fp8_gemm_dgrad_t."""
     N, K = wq.shape
     _expect(wq, "wq", torch.uint8, (N, K))
     _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
@@ -243,6 +244,22 @@ def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):
     _expect(dx, "dx", torch.bfloat16, (T, K))
     _check(lib().fp8_gemm_dgrad(_ptr(dyq), _ptr(sdy), _ptr(wq), _ptr(sw), T, N, K, _ptr(dx), _stream(stream)),
            "fp8_gemm_dgrad")
+    return dx
+
+
+def fp8_gemm_dgrad_t(dyq, sdy, wqT, swT, out=None, stream=None):
+    """dX[T,K] bf16 = dY W from 1x128-quantized dY [T,N] and the transposed
+    weight copy (fp8_weight_transpose): wqT [K,N], swT [K/128,N/128]."""
+    T, N = dyq.shape
+    K = wqT.shape[0]
+    _expect(dyq, "dyq", torch.uint8, (T, N))
+    _expect(sdy, "sdy", torch.float32, (T, N // GROUP))
+    _expect(wqT, "wqT", torch.uint8, (K, N))
+    _expect(swT, "swT", torch.float32, (K // GROUP, N // GROUP))
+    dx = out if out is not None else _empty((T, K), torch.bfloat16, dyq)
+    _expect(dx, "dx", torch.bfloat16, (T, K))
+    _check(lib().fp8_gemm_dgrad_t(_ptr(dyq), _ptr(sdy), _ptr(wqT), _ptr(swT), T, N, K, _ptr(dx), _stream(stream)),
+           "fp8_gemm_dgrad_t")
     return dx
 
 

@@ -374,6 +374,13 @@ fp8lin_status fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t
     return end_launch();
 }
 
+fp8lin_status fp8_gemm_dgrad_t(const uint8_t* dyq, const float* sdy, const uint8_t* wqT, const float* swT,
+                               int64_t T, int64_t N, int64_t K, void* dx, void* stream)
+{
+    // the forward product of dY [T,N] with the rows of W^T [K,N]
+    return fp8_gemm_fwd(dyq, sdy, wqT, swT, T, K, N, dx, stream);
+}
+
 fp8lin_status fp8_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,
                              int64_t N, int64_t K, int64_t T, void* dw, void* stream)
 {

@@ -122,10 +122,10 @@ fp8lin_status fp8_quant_weight(const void* w, int64_t N, int64_t K,
  *   wq  : uint8 [N,K], sw : float [N/128][K/128]   (input, fp8_quant_weight)
  *   wqT : uint8 [K,N], swT : float [K/128][N/128]  (output)
  *   wqT[k][n] = wq[n][k], swT[j][i] = sw[i][j].
- * With it, DGrad is the forward GEMM on the transposed weight:
- *   fp8_gemm_fwd(dyq, sdy, wqT, swT, T, K, N, dx)
- * computes the same sums as fp8_gemm_dgrad(dyq, sdy, wq, sw, T, N, K, dx)
- * (up to fp32 summation order) with both operands contraction-contiguous.
+ * With it, fp8_gemm_dgrad_t(dyq, sdy, wqT, swT, T, N, K, dx) computes the
+ * same sums as fp8_gemm_dgrad(dyq, sdy, wq, sw, T, N, K, dx) (up to fp32
+ * summation order) as the forward GEMM on the transposed weight, with both
+ * operands contiguous along the contraction.
  * N % 128 == 0 and K % 128 == 0.  N == 0 or K == 0 is an OK no-op.
  */
 fp8lin_status fp8_weight_transpose(const uint8_t* wq, const float* sw, int64_t N, int64_t K,
@@ -209,6 +209,20 @@ fp8lin_status fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy,
                              const uint8_t* wq, const float* sw,
                              int64_t T, int64_t N, int64_t K,
                              void* dx, void* stream);
+
+/*
+ * DGrad on the transposed weight (the fast path):  dX = dY W from
+ * fp8_weight_transpose's copy, the same sums as fp8_gemm_dgrad with both
+ * operands contiguous along the contraction.
+ *   dX[t,k] = sum_g sdy[t][g] * swT[k/128][g] * sum_{n in g} dec(dyq[t,n]) dec(wqT[k,n])
+ *   dyq : [T,N], sdy : [T][N/128];  wqT : [K,N], swT : [K/128][N/128]
+ *   dx  : BF16 [T,K] (output).
+ * Shapes, errors and empty cases as fp8_gemm_dgrad.
+ */
+fp8lin_status fp8_gemm_dgrad_t(const uint8_t* dyq, const float* sdy,
+                               const uint8_t* wqT, const float* swT,
+                               int64_t T, int64_t N, int64_t K,
+                               void* dx, void* stream);
 
 /*
  * WGrad GEMM (NT over tokens):  dW = dY^T X.

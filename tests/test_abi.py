@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert len(names) >= 11, names
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
-              "fp8_linear_fwd", "fp8_weight_transpose", "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_linear_fwd", "fp8_weight_transpose", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -121,6 +121,9 @@ def test_gemm_validation(L):
     assert L.fp8_gemm_dgrad(A, B, C, D, 4, 100, 128, E, s0) == SHAPE
     assert L.fp8_gemm_dgrad(A, B, C, D, 4, 128, 100, E, s0) == SHAPE
     assert L.fp8_gemm_dgrad(None, None, None, None, 0, 128, 128, None, s0) == OK
+    assert L.fp8_gemm_dgrad_t(A, B, C, D, 4, 100, 128, E, s0) == SHAPE
+    assert L.fp8_gemm_dgrad_t(A, B, C, D, 4, 128, 128, C, s0) == ALIAS
+    assert L.fp8_gemm_dgrad_t(None, None, None, None, 0, 128, 128, None, s0) == OK
     assert L.fp8_gemm_wgrad(A, B, C, D, 5, 7, 100, E, s0) == SHAPE                 # T % 128
     assert L.fp8_gemm_wgrad(A, B, C, D, 5, 7, 128, A, s0) == ALIAS
     assert L.fp8_gemm_wgrad(None, None, None, None, 5, 0, 128, None, s0) == OK

@@ -241,8 +241,10 @@ def test_dgrad_via_transposed_weight(T, N, K):
     say("weight transpose + fwd as dgrad", T, N, K)
     wqT, swT = fl.fp8_weight_transpose(u8_to_dev(wq), f32_to_dev(sw))
     assert np.array_equal(host(wqT), wq.T) and np.array_equal(host(swT), sw.T)
-    dx = fl.fp8_gemm_fwd(u8_to_dev(dyq), f32_to_dev(sdy), wqT, swT)
+    dx = fl.fp8_gemm_dgrad_t(u8_to_dev(dyq), f32_to_dev(sdy), wqT, swT)
     check_metric(host(dx), oracle.gemm_dgrad(dyq, sdy, wq, sw), "dgrad(wT) %dx%dx%d" % (T, N, K))
+    same = fl.fp8_gemm_fwd(u8_to_dev(dyq), f32_to_dev(sdy), wqT, swT)
+    assert np.array_equal(host(dx), host(same))
 
 
 # -------------------------------------------------------------------- WGrad
@@ -337,7 +339,7 @@ def test_backward_full_size_sampled():
     dx = fl.fp8_gemm_dgrad(dyq, sdy, wq, sw)
     say("backward full: dgrad on the transposed weight")
     wqT, swT = fl.fp8_weight_transpose(wq, sw)
-    dx_t = fl.fp8_gemm_fwd(dyq, sdy, wqT, swT)
+    dx_t = fl.fp8_gemm_dgrad_t(dyq, sdy, wqT, swT)
     del wqT, swT
     say("backward full: wgrad")
     dw = fl.fp8_gemm_wgrad(dyTq, sdyT, xTq, sxT)
