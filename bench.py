@@ -7,8 +7,9 @@ A step is one pass of the layer's hot path over one batch of synthetic
 inputs already resident in HBM:
   decode   (default) 8B-shaped MLP up-proj rollout step: 1x128 quantization of
            X [64,4096] + block-scaled GEMM against W [14336,4096] quantized
-           128x128 beforehand (as rollout does between optimizer steps);
-           8 weight copies are rotated so the weights come from HBM, not MALL
+           128x128 (and put in the decode layout, fp8_weight_pack) beforehand,
+           as rollout does between optimizer steps; 10 weight copies are
+           rotated so the weights come from HBM, not MALL
   prefill  7B-shaped forward: quantize X [8192,3584] and W [18944,3584], GEMM
   large    32B-shaped forward: quantize X [16384,5120] and W [27648,5120], GEMM
   backward 8B-shaped backward: dual transpose-quant of dY [8192,14336],
@@ -113,12 +114,13 @@ def build_step(name, torch, fl, synthetic):
             wqs = []
             for r in range(st.rotate):
                 wq, sw = fl.fp8_quant_weight(w)
-                wqs.append((wq, sw))
+                wqs.append((fl.fp8_weight_pack(wq), sw))   # decode layout, made with the quantization
+                del wq
             torch.cuda.synchronize()
             del w
             st.add("quant_act", lambda i: fl.fp8_quant_act(x, out=(xq, sx)), "hbm", act_quant_bytes(M, K))
-            st.add("gemm_fwd", lambda i: fl.fp8_gemm_fwd(xq, sx, wqs[i % st.rotate][0], wqs[i % st.rotate][1],
-                                                          out=y),
+            st.add("gemm_fwd", lambda i: fl.fp8_gemm_fwd_packed(xq, sx, wqs[i % st.rotate][0], wqs[i % st.rotate][1],
+                                                                 out=y),
                    "hbm", gemm_bytes(M, N, K, (N // G) * (K // G)))
             st.dominant = "gemm_fwd"
         else:
@@ -130,6 +132,8 @@ def build_step(name, torch, fl, synthetic):
         st.gemm_flop = 2 * M * N * K
         st.config = {"workload": wl.doc, "M": M, "N": N, "K": K, "outlier_columns": wl.n_out,
                      "weight_copies_rotated": st.rotate}
+        if name == "decode":
+            st.config["weight_layout"] = "decode layout (fp8_weight_pack), made with the weight quantization"
     else:
         T, N, K = wl.M, wl.N, wl.K
         dy = bf16(synthetic.grad_out(T, N, seed=0))

@@ -20,8 +20,8 @@ import torch
 
 __all__ = [
     "lib", "Fp8LinError", "GROUP",
-    "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_quant_transpose",
-    "fp8_gemm_fwd", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
+    "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
+    "fp8_gemm_fwd", "fp8_gemm_fwd_packed", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -44,6 +44,9 @@ _SYMBOLS = {
                           ctypes.c_void_p], ctypes.c_int),
     "fp8_weight_transpose": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                               ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "fp8_weight_pack": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p],
+                        ctypes.c_int),
+    "fp8_gemm_fwd_packed": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_quant_transpose": ([ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p], ctypes.c_int),
@@ -161,6 +164,17 @@ def fp8_weight_transpose(wq: torch.Tensor, sw: torch.Tensor, out=None, stream=No
     return qT, sT
 
 
+def fp8_weight_pack(wq: torch.Tensor, out=None, stream=None):
+    """Decode layout of quantized weight codes u8 [N,K] (same bytes, reordered;
+    a u8 tensor of shape [N,K]) for fp8_gemm_fwd_packed."""
+    N, K = wq.shape
+    _expect(wq, "wq", torch.uint8, (N, K))
+    wqp = out if out is not None else _empty((N, K), torch.uint8, wq)
+    _expect(wqp, "wqp", torch.uint8, (N, K))
+    _check(lib().fp8_weight_pack(_ptr(wq), N, K, _ptr(wqp), _stream(stream)), "fp8_weight_pack")
+    return wqp
+
+
 def fp8_quant_transpose(src: torch.Tensor, src_scales: torch.Tensor | None = None, dual: bool = False,
                         out=None, stream=None):
     """128-along-T quantization written transposed (WGrad operands).
@@ -208,6 +222,21 @@ def fp8_gemm_fwd(xq, sx, wq, sw, out=None, stream=None):
     _expect(y, "y", torch.bfloat16, (M, N))
     _check(lib().fp8_gemm_fwd(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
            "fp8_gemm_fwd")
+    return y
+
+
+def fp8_gemm_fwd_packed(xq, sx, wqp, sw, out=None, stream=None):
+    """Y[M,N] bf16 = X W^T for M <= 64 from the decode layout wqp = fp8_weight_pack(wq)."""
+    M, K = xq.shape
+    N = wqp.shape[0]
+    _expect(xq, "xq", torch.uint8, (M, K))
+    _expect(sx, "sx", torch.float32, (M, K // GROUP))
+    _expect(wqp, "wqp", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    y = out if out is not None else _empty((M, N), torch.bfloat16, xq)
+    _expect(y, "y", torch.bfloat16, (M, N))
+    _check(lib().fp8_gemm_fwd_packed(_ptr(xq), _ptr(sx), _ptr(wqp), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
+           "fp8_gemm_fwd_packed")
     return y
 
 

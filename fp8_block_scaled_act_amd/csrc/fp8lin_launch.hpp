@@ -21,6 +21,11 @@ void launch_decode_probe(const uint8_t* in, int64_t n, float* out, int method, h
 void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st);
 void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                      int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
+// Decode layout of W (fp8_weight_pack) and the forward GEMM on it
+// (M <= 64, K % 256 == 0, K <= 16384).
+void launch_pack_decode(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, hipStream_t st);
+void launch_gemm_fwd_packed(const uint8_t* xq, const float* sx, const uint8_t* wqp, const float* sw,
+                            int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
 void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
                        int64_t T, int64_t N, int64_t K, void* dx, hipStream_t st);
 void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,

@@ -711,6 +711,76 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Requires M <= 64, G = K / 128 even and G <= GM; every role passes
 // 3 + G / 2 barriers.
+// Scale products sx[r][g] * sw[g] of a 64-column block (the columns lie in
+// one 128-column weight block), four per thread per batch with the batch's
+// loads in flight together; rows past M repeat row M - 1.  Threads 0..511.
+__device__ __forceinline__ void decode_scale_table(const GemmArgs& p, int64_t n0, int64_t G, int GP, int tid,
+                                                   float* lds_ps)
+{
+    const float* swp = p.sb + (n0 / kGroup) * G;
+    const int nps = 64 * (int)G;
+    for (int base = 0; base < nps; base += 512 * 4) {
+        float sv[4], wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = min(base + tid + 512 * i, nps - 1);
+            const int row = idx / (int)G, g = idx - row * (int)G;
+            const int64_t xrow = row < p.M ? row : p.M - 1;
+            sv[i] = p.sa[xrow * G + g];
+            wv[i] = swp[g];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = base + tid + 512 * i;
+            if (idx < nps) {
+                const int row = idx / (int)G, g = idx - row * (int)G;
+                lds_ps[row * GP + g] = sv[i] * wv[i];
+            }
+        }
+    }
+}
+
+// Adds the four (kp, kq) partial sums of the eight MMA waves in a fixed order
+// through `red` (an idle LDS ring, >= 48 KB) and stores the 64 x 64 block of
+// Y as bf16.  Passes one barrier.
+__device__ __forceinline__ void decode_reduce_store(const GemmArgs& p, v16f (&acc)[2], float* red, int64_t n0,
+                                                    int ct, int kp, int kq, int m, int kh, int lane)
+{
+    const int part = kp * 2 + kq;
+    if (part != 0) {
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[(((part - 1) * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane] = acc[xt][r];
+    }
+    __syncthreads();
+    if (part == 0) {
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt) {
+            const int64_t row = 32 * xt + m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int pp = 0; pp < 3; ++pp)
+                    acc[xt][r] += red[((pp * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane];
+            if (row < p.M) {
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    uint32_t v[2];
+#pragma unroll
+                    for (int b2 = 0; b2 < 2; ++b2) {
+                        const int r0 = 4 * a4 + 2 * b2;
+                        v[b2] = (uint32_t)f32_to_bf16_rne(acc[xt][r0]) |
+                                ((uint32_t)f32_to_bf16_rne(acc[xt][r0 + 1]) << 16);
+                    }
+                    *reinterpret_cast<u32x2*>(p.c + row * p.N + n0 + 32 * ct + 8 * a4 + 4 * kh) = u32x2{v[0], v[1]};
+                }
+            }
+        }
+    }
+}
+
 template <int WDW, int WDX, int GM>
 __global__ __launch_bounds__(640) void gemm_fwd_decode_kernel(const GemmArgs p)
 {
@@ -727,30 +797,7 @@ __global__ __launch_bounds__(640) void gemm_fwd_decode_kernel(const GemmArgs p)
     const int64_t n0 = (int64_t)blockIdx.x * 64;
 
     if (wave < 8) {
-        {
-            // scale products, four per thread per batch with the batch's loads in flight together
-            const float* swp = p.sb + (n0 / kGroup) * G;
-            const int nps = 64 * (int)G;
-            for (int base = 0; base < nps; base += 512 * 4) {
-                float sv[4], wv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int idx = min(base + tid + 512 * i, nps - 1);
-                    const int row = idx / (int)G, g = idx - row * (int)G;
-                    const int64_t xrow = row < p.M ? row : p.M - 1;
-                    sv[i] = p.sa[xrow * G + g];
-                    wv[i] = swp[g];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int idx = base + tid + 512 * i;
-                    if (idx < nps) {
-                        const int row = idx / (int)G, g = idx - row * (int)G;
-                        lds_ps[row * GP + g] = sv[i] * wv[i];
-                    }
-                }
-            }
-        }
+        decode_scale_table(p, n0, G, GP, tid, lds_ps);
         const int ct = wave & 1, kp = (wave >> 1) & 1, kq = wave >> 2;
         const int m = lane & 31, kh = lane >> 5;
         const int wr = 32 * ct + m;
@@ -799,44 +846,142 @@ __global__ __launch_bounds__(640) void gemm_fwd_decode_kernel(const GemmArgs p)
             __syncthreads();                       // chunk c drained, chunk c + 1 landed
         }
         __syncthreads();                           // both loaders drained: the X ring is idle
-        float* red = reinterpret_cast<float*>(&lds_x[0][0]);
-        const int part = kp * 2 + kq;
-        if (part != 0) {
-#pragma unroll
-            for (int xt = 0; xt < 2; ++xt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    red[(((part - 1) * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane] = acc[xt][r];
-        }
-        __syncthreads();
-        if (part == 0) {
-#pragma unroll
-            for (int xt = 0; xt < 2; ++xt) {
-                const int64_t row = 32 * xt + m;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-#pragma unroll
-                    for (int pp = 0; pp < 3; ++pp)
-                        acc[xt][r] += red[((pp * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane];
-                if (row < p.M) {
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-                        uint32_t v[2];
-#pragma unroll
-                        for (int b2 = 0; b2 < 2; ++b2) {
-                            const int r0 = 4 * a4 + 2 * b2;
-                            v[b2] = (uint32_t)f32_to_bf16_rne(acc[xt][r0]) |
-                                    ((uint32_t)f32_to_bf16_rne(acc[xt][r0 + 1]) << 16);
-                        }
-                        *reinterpret_cast<u32x2*>(p.c + row * p.N + n0 + 32 * ct + 8 * a4 + 4 * kh) = u32x2{v[0], v[1]};
-                    }
-                }
-            }
-        }
+        decode_reduce_store(p, acc, reinterpret_cast<float*>(&lds_x[0][0]), n0, ct, kp, kq, m, kh, lane);
     } else if (wave == 8) {
         stream_operand<WDW>(p.b, p.N, n0, p.Kc, nch, (uint32_t)(uintptr_t)&lds_w[0][0], lane);
     } else {
         stream_operand<WDX>(p.a, p.M, 0, p.Kc, nch, (uint32_t)(uintptr_t)&lds_x[0][0], lane);
+    }
+}
+
+// ------------------------------------------- decode with a fragment-packed W
+//
+// The same product for <= 64 rows, with W in the decode layout written by
+// fp8_weight_pack: for each 64-row block nb, chunk c (256 columns) and MMA
+// wave w = ct + 2 kp + 4 kq, the 2 KB that wave multiplies are contiguous,
+// ordered [q][lane][16 bytes], lane = m + 32 kh holding piece
+// 8 kp + 4 kh + 2 kq + q of row 32 ct + m (the pieces the LDS version reads).
+// So each MMA wave loads its W fragments with two fully coalesced 1 KB loads
+// per chunk straight into registers, one chunk ahead, and W needs neither LDS
+// nor a loader wave; X still streams through the LDS ring (wave 8).  The
+// arithmetic, and so every result bit, is that of gemm_fwd_decode_kernel.
+// NCH > 0 fixes K / 256 at compile time (fully unrolled loop); NCH == 0 reads
+// it at run time.
+__device__ __forceinline__ int64_t packed_piece(int64_t nb, int64_t nch, int64_t c, int w, int q, int lane)
+{
+    return (((nb * nch + c) * 8 + w) * 2 + q) * 64 + lane;   // in 16-byte pieces
+}
+
+template <int GM, int NCH>
+__global__ __launch_bounds__(576) void gemm_fwd_decode_packed_kernel(const GemmArgs p)
+{
+    using namespace dec;
+    constexpr int WDX = 4;
+    static_assert(WDX * WCH >= 3 * 2 * 2 * 16 * 64 * 4, "partial sums fit in the X ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_x[WDX][WCH];
+    __shared__ __attribute__((aligned(16))) float lds_ps[64 * (GM + 1)];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t G = p.Kc / kGroup, nch = NCH > 0 ? NCH : G / CH;
+    const int GP = (int)G | 1;
+    const int64_t n0 = (int64_t)blockIdx.x * 64;
+
+    if (wave < 8) {
+        decode_scale_table(p, n0, G, GP, tid, lds_ps);
+        const u32x4* wsrc = reinterpret_cast<const u32x4*>(p.b) + packed_piece(blockIdx.x, nch, 0, wave, 0, lane);
+        u32x4 wreg[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            wreg[q] = __builtin_nontemporal_load(wsrc + q * 64);
+        const int ct = wave & 1, kp = (wave >> 1) & 1, kq = wave >> 2;
+        const int m = lane & 31, kh = lane >> 5;
+        v16f acc[2];
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[xt][r] = 0.f;
+        __syncthreads();                           // chunk 0 of X landed, table built
+        constexpr int kUnroll = NCH > 0 ? NCH : 1;
+#pragma unroll kUnroll
+        for (int64_t c = 0; c < nch; ++c) {
+            const uint8_t* xl = lds_x[c % WDX];
+            u32x4 xv[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt)
+                    xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
+            v8h wlo[2], whi[2];
+            if constexpr (NCH == 0) {
+                // run-time loop: convert this chunk's W fragments before the
+                // next chunk is loaded into their registers (otherwise the
+                // loop's back edge copies them and waits for the loads)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    wlo[q] = cvt8(wreg[q].x, wreg[q].y);
+                    whi[q] = cvt8(wreg[q].z, wreg[q].w);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const u32x4 wv[2] = {wreg[0], wreg[1]};
+            {
+                const int64_t cn = c + 1 < nch ? c + 1 : c;  // last chunk: a harmless re-read
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    wreg[q] = __builtin_nontemporal_load(wsrc + cn * (8 * 2 * 64) + q * 64);
+            }
+            if constexpr (NCH == 0)
+                __builtin_amdgcn_sched_barrier(0);
+            v16f tmp[2];
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    tmp[xt][r] = 0.f;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if constexpr (NCH > 0) {
+                    wlo[q] = cvt8(wv[q].x, wv[q].y);
+                    whi[q] = cvt8(wv[q].z, wv[q].w);
+                }
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt) {
+                    const v8h xlo = cvt8(xv[xt][q].x, xv[xt][q].y), xhi = cvt8(xv[xt][q].z, xv[xt][q].w);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wlo[q], xlo, tmp[xt], 0, 0, 0);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(whi[q], xhi, tmp[xt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt) {
+                const float sc = lds_ps[(32 * xt + m) * GP + c * CH + kp];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[xt][r] = fmaf(tmp[xt][r], sc, acc[xt][r]);
+            }
+            __syncthreads();                       // chunk c drained, chunk c + 1 landed
+        }
+        __syncthreads();                           // the loader drained: the X ring is idle
+        decode_reduce_store(p, acc, reinterpret_cast<float*>(&lds_x[0][0]), n0, ct, kp, kq, m, kh, lane);
+    } else {
+        stream_operand<WDX>(p.a, p.M, 0, p.Kc, nch, (uint32_t)(uintptr_t)&lds_x[0][0], lane);
+    }
+}
+
+// W codes [N][K] -> the decode layout above, one 16-byte piece per thread
+// (stores coalesced, loads gathered; done once per weight update).
+__global__ __launch_bounds__(256) void pack_decode_kernel(const uint8_t* __restrict__ wq, int64_t K,
+                                                          int64_t npieces, u32x4* __restrict__ wqp)
+{
+    const int64_t nch = K / (dec::CH * kGroup);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < npieces; i += (int64_t)gridDim.x * 256) {
+        const int lane = (int)(i & 63), q = (int)((i >> 6) & 1), w = (int)((i >> 7) & 7);
+        const int64_t c = (i >> 10) % nch, nb = (i >> 10) / nch;
+        const int ct = w & 1, kp = (w >> 1) & 1, kq = w >> 2, m = lane & 31, kh = lane >> 5;
+        const int64_t row = nb * 64 + 32 * ct + m;
+        const int pc = 8 * kp + 4 * kh + 2 * kq + q;
+        wqp[i] = *reinterpret_cast<const u32x4*>(wq + row * K + c * (dec::CH * kGroup) + 16 * pc);
     }
 }
 
@@ -1144,6 +1289,34 @@ void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, cons
         launch_gemm<64, 64, 1, 4, Mode::Fwd>(p, st);
     else
         launch_gemm_nt<Mode::Fwd>(p, st);
+}
+
+void launch_pack_decode(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, hipStream_t st)
+{
+    const int64_t npieces = N * K / 16;
+    int64_t b = (npieces + 255) / 256;
+    if (b > 65536)
+        b = 65536;
+    pack_decode_kernel<<<(unsigned)b, 256, 0, st>>>(wq, K, npieces, reinterpret_cast<u32x4*>(wqp));
+}
+
+void launch_gemm_fwd_packed(const uint8_t* xq, const float* sx, const uint8_t* wqp, const float* sw, int64_t M,
+                            int64_t N, int64_t K, void* y, hipStream_t st)
+{
+    GemmArgs p{xq, sx, wqp, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
+    const int64_t nch = K / (dec::CH * kGroup);
+    const unsigned grid = (unsigned)(N / 64);
+    // the model widths of the decode workloads get a fully unrolled loop
+    if (nch == 14)
+        gemm_fwd_decode_packed_kernel<64, 14><<<grid, 576, 0, st>>>(p);
+    else if (nch == 16)
+        gemm_fwd_decode_packed_kernel<64, 16><<<grid, 576, 0, st>>>(p);
+    else if (nch == 20)
+        gemm_fwd_decode_packed_kernel<64, 20><<<grid, 576, 0, st>>>(p);
+    else if (nch <= 32)
+        gemm_fwd_decode_packed_kernel<64, 0><<<grid, 576, 0, st>>>(p);
+    else
+        gemm_fwd_decode_packed_kernel<128, 0><<<grid, 576, 0, st>>>(p);
 }
 
 void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t T,

@@ -176,6 +176,36 @@ fp8lin_status fp8_gemm_fwd(const uint8_t* xq, const float* sx,
                            void* y, void* stream);
 
 /*
+ * Decode layout of a quantized weight (once per optimizer step, next to
+ * fp8_quant_weight), for rollout GEMMs with at most 64 rows.  Jet-RL
+ * summary, "Core architecture" (rollout on the same FP8 weights as
+ * training; only the byte order of the codes changes, not a value).
+ *   wq  : uint8 [N,K]  (input, fp8_quant_weight's codes)
+ *   wqp : uint8, N*K bytes (output): for each 64-row block, each 256-column
+ *         chunk and each of the 8 matrix waves of the decode kernel, the 2 KB
+ *         that wave multiplies, in the order its lanes load them.
+ * The scales are not moved (fp8_gemm_fwd_packed takes fp8_quant_weight's sw).
+ * N % 128 == 0 and K % 256 == 0.  N == 0 or K == 0 is an OK no-op.
+ */
+fp8lin_status fp8_weight_pack(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, void* stream);
+
+/*
+ * Forward / rollout GEMM on the decode layout:  Y = X W^T, exactly the sums
+ * (and bits) of fp8_gemm_fwd on the unpacked codes, for M <= 64.  Each
+ * matrix wave loads its weight fragments with fully coalesced loads straight
+ * into registers instead of staging them through LDS.
+ *   xq : [M,K], sx : [M][K/128], wqp : fp8_weight_pack of wq [N,K],
+ *   sw : [N/128][K/128], y : BF16 [M,N] (output).
+ * 0 <= M <= 64, N % 128 == 0, K % 256 == 0 and K <= 16384
+ * (FP8LIN_ERR_SHAPE otherwise).  M == 0 or N == 0 is an OK no-op; K == 0
+ * writes zeros.
+ */
+fp8lin_status fp8_gemm_fwd_packed(const uint8_t* xq, const float* sx,
+                                  const uint8_t* wqp, const float* sw,
+                                  int64_t M, int64_t N, int64_t K,
+                                  void* y, void* stream);
+
+/*
  * One forward / rollout linear step from BF16 activations, in one call:
  *   fp8_quant_act(x) -> (xq, sx), then y = fp8_gemm_fwd(xq, sx, wq, sw),
  * enqueued as those two kernels on the stream.

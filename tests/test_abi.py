@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert len(names) >= 11, names
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
-              "fp8_linear_fwd", "fp8_weight_transpose", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
+              "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -158,6 +159,22 @@ def test_weight_transpose_validation(L):
     assert L.fp8_weight_transpose(A, B, 128, 128, C + 4, D, s0) == ALIGN
     assert L.fp8_weight_transpose(None, None, 0, 128, None, None, s0) == OK
     assert L.fp8_weight_transpose(A, B, 128, 128, C, D, s0) == DEVICE
+
+
+@fake_ptrs
+def test_packed_decode_validation(L):
+    assert L.fp8_weight_pack(A, 128, 128, B, s0) == SHAPE               # K % 256
+    assert L.fp8_weight_pack(A, 64, 256, B, s0) == SHAPE                # N % 128
+    assert L.fp8_weight_pack(A, 128, 256, A, s0) == ALIAS
+    assert L.fp8_weight_pack(None, 0, 256, None, s0) == OK
+    assert L.fp8_weight_pack(A, 128, 256, B, s0) == DEVICE
+    # xq, sx, wqp, sw, M, N, K, y
+    assert L.fp8_gemm_fwd_packed(A, B, C, D, 65, 128, 256, E, s0) == SHAPE    # M > 64
+    assert L.fp8_gemm_fwd_packed(A, B, C, D, 4, 128, 384, E, s0) == SHAPE     # K % 256
+    assert L.fp8_gemm_fwd_packed(A, B, C, D, 4, 128, 16640, E, s0) == SHAPE   # K > 16384
+    assert L.fp8_gemm_fwd_packed(A, B, C, D, 4, 128, 256, C, s0) == ALIAS
+    assert L.fp8_gemm_fwd_packed(None, None, None, None, 0, 128, 256, None, s0) == OK
+    assert L.fp8_gemm_fwd_packed(A, B, C, D, 4, 128, 256, E, s0) == DEVICE
 
 
 @fake_ptrs

@@ -77,6 +77,50 @@ def test_fwd_decode_shapes(M, N, K):
     check_metric(host(y), oracle.gemm_fwd(xq, sx, wq, sw), "fwd %dx%dx%d" % (M, N, K))
 
 
+def pack_reference(wq: np.ndarray) -> np.ndarray:
+    """The decode layout written out from its definition: for each 64-row
+    block, 256-column chunk, matrix wave w = ct + 2 kp + 4 kq, q and lane
+    (m + 32 kh): the 16 codes of row 32 ct + m at chunk piece 8 kp + 4 kh + 2 kq + q."""
+    N, K = wq.shape
+    nch = K // 256
+    out = np.empty(N * K, np.uint8)
+    i = 0
+    for nb in range(N // 64):
+        for c in range(nch):
+            for w in range(8):
+                ct, kp, kq = w & 1, (w >> 1) & 1, w >> 2
+                for q in range(2):
+                    for lane in range(64):
+                        m, kh = lane & 31, lane >> 5
+                        pc = 8 * kp + 4 * kh + 2 * kq + q
+                        out[i:i + 16] = wq[nb * 64 + 32 * ct + m, c * 256 + 16 * pc: c * 256 + 16 * pc + 16]
+                        i += 16
+    return out.reshape(N, K)
+
+
+@pytest.mark.parametrize("N,K", [(128, 256), (256, 768)])
+def test_weight_pack_layout(N, K):
+    wq = synthetic.random_codes((N, K), N + K, 61)
+    say("weight pack", N, K)
+    assert np.array_equal(host(fl.fp8_weight_pack(u8_to_dev(wq))), pack_reference(wq))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (17, 256, 768), (64, 384, 2048), (33, 256, 3584),
+                                   (64, 14336, 4096), (5, 128, 5120), (64, 512, 16384), (40, 128, 1024)])
+def test_fwd_packed_matches_unpacked(M, N, K):
+    """The decode kernel on the packed layout computes the same bits as the
+    forward GEMM on the unpacked codes (unrolled widths 3584/4096/5120 and the
+    run-time loop), and stays within the tolerance of the oracle."""
+    xq, sx = codes_scales((M, K), (M, K // G), M * 5 + K, 62)
+    wq, sw = codes_scales((N, K), (N // G, K // G), N * 3 + K, 63)
+    say("gemm_fwd_packed", M, N, K)
+    xd, sxd, wd, swd = u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw)
+    y = host(fl.fp8_gemm_fwd_packed(xd, sxd, fl.fp8_weight_pack(wd), swd))
+    assert np.array_equal(y, host(fl.fp8_gemm_fwd(xd, sxd, wd, swd)))
+    if N * K <= 4096 * 4096:
+        check_metric(y, oracle.gemm_fwd(xq, sx, wq, sw), "fwd packed %dx%dx%d" % (M, N, K))
+
+
 def test_fwd_one_hot_every_code():
     """Pins MFMA operand decoding and the fragment/output layouts: W holds every
     finite code once in column 0 of its group; X is one-hot at that column."""
@@ -315,6 +359,11 @@ def test_fwd_full_size_sampled(name, M, N, K):
     y = fl.fp8_gemm_fwd(xq, sx, wq, sw)
     rows = sampled_rows(M)
     yg = host(y[torch.from_numpy(rows).to(DEV)])
+    if M <= 64:
+        # the decode step as timed: packed weight layout
+        yp = fl.fp8_gemm_fwd_packed(xq, sx, fl.fp8_weight_pack(wq), sw)
+        assert np.array_equal(host(yp), host(y))
+        del yp
     del y, xq, sx, wq, sw
     torch.cuda.empty_cache()
     oxq, osx = oracle.quant_act(x[rows])
