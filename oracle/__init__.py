@@ -64,10 +64,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_dequant_rowgroup.argtypes = [u8p, f32p, i64, i64, f64p]
         L.oracle_dequant_block.argtypes = [u8p, f32p, i64, i64, f64p]
         L.oracle_gemm.argtypes = [i64, i64, i64, f64p, i64, i64, f64p, i64, i64, f64p]
+        L.oracle_rmsnorm_bf16.argtypes = [u16p, u16p, i64, i64, ctypes.c_float, u16p, f32p]
+        L.oracle_swiglu_bf16.argtypes = [u16p, u16p, i64, i64, i64, u16p, u8p]
         L.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_quant_act", "oracle_quant_weight", "oracle_quant_transpose_bf16",
                   "oracle_quant_transpose_fp8", "oracle_dequant_rowgroup",
-                  "oracle_dequant_block", "oracle_gemm"):
+                  "oracle_dequant_block", "oracle_gemm", "oracle_rmsnorm_bf16",
+                  "oracle_swiglu_bf16"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -156,6 +159,57 @@ def quant_transpose_fp8(q: np.ndarray, s_row: np.ndarray):
     lib().oracle_quant_transpose_fp8(_ptr(q, ctypes.c_uint8), _ptr(s_row, ctypes.c_float), T, C,
                                      _ptr(qT, ctypes.c_uint8), _ptr(sT, ctypes.c_float))
     return qT, sT
+
+
+# ----------------------------------------------------- producer operators
+
+def rmsnorm_bf16(x_bf16: np.ndarray, gamma_bf16: np.ndarray, eps: float):
+    """RMSNorm of bf16 rows: x [M,K], gamma [K] -> (y bf16 bits [M,K], rstd f32 [M]).
+
+    fp64 sum of squares (tree per 128-group, groups ascending), r = 1/sqrt(ss/K + eps)
+    in fp64, rstd = fp32(r), y = bf16(fp32(fp32(x * rstd) * gamma))."""
+    x = _bits16(x_bf16)
+    g = _bits16(gamma_bf16)
+    M, K = x.shape
+    assert K % GROUP == 0 and g.shape == (K,)
+    y = np.empty((M, K), np.uint16)
+    r = np.empty((M,), np.float32)
+    lib().oracle_rmsnorm_bf16(_ptr(x, ctypes.c_uint16), _ptr(g, ctypes.c_uint16), M, K, float(eps),
+                              _ptr(y, ctypes.c_uint16), _ptr(r, ctypes.c_float))
+    return y, r
+
+
+def swiglu_bf16(gate_bf16: np.ndarray, up_bf16: np.ndarray):
+    """SwiGLU of bf16 tensors [M,F]: h = bf16(silu(g) * u), evaluated in fp64.
+
+    Returns (h bf16 bits [M,F], near_tie bool [M,F]); near_tie marks elements
+    whose fp64 value lies within 2^-44 (relative) of a bf16 rounding midpoint,
+    where either bf16 neighbour is a correct result."""
+    g = _bits16(gate_bf16)
+    u = _bits16(up_bf16)
+    assert g.shape == u.shape and g.ndim == 2
+    M, F = g.shape
+    h = np.empty((M, F), np.uint16)
+    t = np.empty((M, F), np.uint8)
+    lib().oracle_swiglu_bf16(_ptr(g, ctypes.c_uint16), _ptr(u, ctypes.c_uint16), F, M, F,
+                             _ptr(h, ctypes.c_uint16), _ptr(t, ctypes.c_uint8))
+    return h, t.astype(bool)
+
+
+def rmsnorm_quant(x_bf16: np.ndarray, gamma_bf16: np.ndarray, eps: float):
+    """RMSNorm followed by 1x128 quantization of its bf16 output:
+    -> (q u8 [M,K], s f32 [M,K/128], rstd f32 [M])."""
+    y, r = rmsnorm_bf16(x_bf16, gamma_bf16, eps)
+    q, s = quant_act(y)
+    return q, s, r
+
+
+def swiglu_quant(gate_bf16: np.ndarray, up_bf16: np.ndarray):
+    """SwiGLU followed by 1x128 quantization of its bf16 output:
+    -> (q u8 [M,F], s f32 [M,F/128], near_tie bool [M,F])."""
+    h, t = swiglu_bf16(gate_bf16, up_bf16)
+    q, s = quant_act(h)
+    return q, s, t
 
 
 # ------------------------------------------------------------- dequantize

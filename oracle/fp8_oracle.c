@@ -25,6 +25,10 @@
  * (no FMA contraction, no flush-to-zero, IEEE single division).  OpenMP is
  * used only across independent rows, so results do not depend on threads.
  *
+ * It also holds the two producer operators that feed a linear layer (RMSNorm
+ * and SwiGLU, section "Implementation": fused activation / RMSNorm kernels),
+ * whose BF16 outputs are then quantized by the 1x128 activation quantizer.
+ *
  * Every function below is pinned by a CPU test against something other than
  * itself (exhaustive brute force, closed forms, exact rationals or an
  * independent library routine), except the FP8-source transpose-quant, whose
@@ -294,6 +298,102 @@ void oracle_gemm(int64_t M, int64_t N, int64_t K,
             for (int64_t k = 0; k < K; ++k)
                 acc += A[m * sam + k * sak] * B[n * sbn + k * sbk];
             C[m * N + n] = acc;
+        }
+}
+
+/* ------------------------------------------------ producer operators
+ *
+ * The summary's "Quantization scheme" section keeps the activations saved for
+ * the backward pass in FP8, produced fused with the operator in front of the
+ * linear layer, and "Implementation" names fused activation and RMSNorm
+ * kernels.  The pages define neither operator.  The oracle takes their
+ * textbook forms with every precision fixed, so that the fused result is the
+ * producer's BF16 output (tensors between operators stay BF16) quantized by
+ * oracle_quant_act:
+ *   RMSNorm:  y = x * r * gamma,  r = 1 / sqrt(mean(x^2) + eps)
+ *   SwiGLU:   h = silu(g) * u,    silu(g) = g / (1 + exp(-g))
+ */
+
+/* Sum of 2^j consecutive fp64 values as a balanced binary tree: the left half
+ * and the right half are summed the same way, then added. */
+static double tree_sum(const double* v, int n)
+{
+    if (n == 1)
+        return v[0];
+    return tree_sum(v, n / 2) + tree_sum(v + n / 2, n / 2);
+}
+
+/*
+ * RMSNorm of BF16 rows, BF16 output.  Per row of K (K % 128 == 0):
+ *   ss   = sum of x^2 in fp64 (each square is exact); each 128-element group
+ *          is summed as a balanced binary tree, then the group sums are added
+ *          in ascending group order starting from 0;
+ *   r    = 1 / sqrt(ss / K + eps), three IEEE fp64 operations and sqrt;
+ *   rstd = fp32(r) (round to nearest even);
+ *   y[k] = bf16_rne(fp32(fp32(x[k] * rstd) * gamma[k])), two fp32 multiplies.
+ * eps >= 0; a row with ss / K + eps == 0 is outside the contract.
+ */
+void oracle_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                         uint16_t* y, float* rstd)
+{
+    int64_t G = K / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * K;
+        double sq[GROUP];
+        double ss = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            for (int i = 0; i < GROUP; ++i) {
+                double v = (double)oracle_bf16_to_f32(row[g * GROUP + i]);
+                sq[i] = v * v;
+            }
+            ss += tree_sum(sq, GROUP);
+        }
+        double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+        float rs = (float)r;
+        if (rstd)
+            rstd[m] = rs;
+        for (int64_t k = 0; k < K; ++k) {
+            float t = oracle_bf16_to_f32(row[k]) * rs;            /* fp32 multiply */
+            float u = t * oracle_bf16_to_f32(gamma[k]);           /* fp32 multiply */
+            y[m * K + k] = oracle_f64_to_bf16((double)u);         /* exact widening, one RNE */
+        }
+    }
+}
+
+/*
+ * SwiGLU of BF16 gate / up rows, BF16 output: h = bf16_rne(v) with
+ * v = (g / (1 + exp(-g))) * u evaluated in fp64 (C library exp, IEEE
+ * division and multiply).  v differs from the exact value by a few fp64 ulps,
+ * which can change the BF16 rounding only when the exact value lies next to
+ * a midpoint between two BF16 neighbours; such elements are flagged in
+ * `near_tie` (|v - midpoint| <= 2^-44 |v|), where either neighbour is a
+ * correct result.  g and u have row stride ld (elements), h is dense [M,F].
+ */
+void oracle_swiglu_bf16(const uint16_t* g, const uint16_t* u, int64_t ld, int64_t M, int64_t F,
+                        uint16_t* h, uint8_t* near_tie)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t f = 0; f < F; ++f) {
+            double gv = (double)oracle_bf16_to_f32(g[m * ld + f]);
+            double uv = (double)oracle_bf16_to_f32(u[m * ld + f]);
+            double v = (gv / (1.0 + exp(-gv))) * uv;
+            h[m * F + f] = oracle_f64_to_bf16(v);
+            uint8_t flag = 0;
+            double a = fabs(v);
+            if (a != 0.0 && isfinite(a)) {
+                int e2;
+                frexp(a, &e2);
+                int E = e2 - 1;
+                if (E < -126)
+                    E = -126;
+                double t = a / ldexp(1.0, E - 7);                 /* exact: a in BF16 quanta */
+                double d = fabs((t - floor(t)) - 0.5);
+                flag = d <= ldexp(t, -44);
+            }
+            if (near_tie)
+                near_tie[m * F + f] = flag;
         }
 }
 

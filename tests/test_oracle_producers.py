@@ -1,0 +1,260 @@
+"""Pins of the oracle's producer operators (RMSNorm and SwiGLU in front of a
+linear layer, each followed by 1x128 quantization of its BF16 output).
+
+The pages only name these operators (fused activation / RMSNorm kernels, FP8
+activations produced fused with the previous operator); the oracle takes the
+textbook forms with the precision of every step fixed.  The pins below check
+it against exact rational arithmetic (Fraction / Decimal), library routines
+(numpy fp32 products, torch's bf16 cast and silu) and closed forms.
+"""
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+import synthetic
+
+G = 128
+
+
+def bf16(a):
+    return synthetic.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def f32(bits):
+    return synthetic.bf16_bits_to_f32(bits)
+
+
+def torch_bf16_bits(a_f32):
+    """fp32 -> bf16 (round to nearest even) through torch's cast."""
+    t = torch.from_numpy(np.ascontiguousarray(a_f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def round_fraction(q: Fraction, mant_bits: int, min_exp: int) -> Fraction:
+    """Nearest value with `mant_bits` significant bits (exponent floor min_exp,
+    i.e. gradual underflow), ties to even, of a rational q."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # now 2^e <= a < 2^(e+1)
+    e = max(e, min_exp)
+    quantum = Fraction(2) ** (e - (mant_bits - 1))
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * quantum
+
+
+def midpoint_distance(q: Fraction, mant_bits: int, min_exp: int) -> Fraction:
+    """|q - nearest rounding midpoint| / |q| for the given format."""
+    a = abs(q)
+    if a == 0:
+        return Fraction(1)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, min_exp)
+    quantum = Fraction(2) ** (e - (mant_bits - 1))
+    n = a / quantum
+    frac = n - (n.numerator // n.denominator)
+    return abs(frac - Fraction(1, 2)) * quantum / a
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+def fp32_inv_sqrt(A: Fraction):
+    """fp32 nearest to 1/sqrt(A) exactly (A > 0), and the relative distance of
+    1/sqrt(A) from the rounding boundary it was closest to."""
+    approx = np.float32(1.0 / math.sqrt(float(A)))
+    c = [approx]
+    for _ in range(3):
+        c.insert(0, np.nextafter(c[0], np.float32(0)))
+        c.append(np.nextafter(c[-1], np.float32(np.inf)))
+    # r >= mid  <=>  mid^2 * A <= 1 ; the candidates bracket r
+    best, margin = None, None
+    for lo, hi in zip(c[:-1], c[1:]):
+        mid = (Fraction(float(lo)) + Fraction(float(hi))) / 2
+        t = mid * mid * A
+        if t <= 1:
+            best = hi                                # r >= mid: hi or beyond
+        elif best is None:
+            best = lo
+        d = abs(t - 1)
+        margin = d if margin is None else min(margin, d)
+    return best, margin
+
+
+def test_rmsnorm_rstd_is_rounded_exact_value():
+    """rstd equals fp32 of the exact 1/sqrt(sum(x^2)/K + eps), computed with
+    rationals: pins the sum of squares (every term, every index), the mean's
+    denominator, where eps enters, the square root and the reciprocal."""
+    M, K = 24, 512
+    x = synthetic.activations(M, K, seed=3, n_out=2)
+    x[5] = bf16(np.linspace(-1e-3, 2e-3, K))                    # small magnitudes
+    x[6] = bf16(np.where(np.arange(K) % 7 == 0, 1e4, 1e-4))    # wide exponent spread
+    gamma = bf16(np.ones(K))
+    for eps in (1e-6, 0.25):
+        _, rstd = oracle.rmsnorm_bf16(x, gamma, eps)
+        xf = f32(x).astype(np.float64)
+        for m in range(M):
+            ss = sum(Fraction(float(v)) ** 2 for v in xf[m])
+            A = ss / K + Fraction(float(np.float32(eps)))
+            want, margin = fp32_inv_sqrt(A)
+            if margin < Fraction(1, 2 ** 40):
+                continue                              # within fp64 evaluation error of a tie
+            assert rstd[m] == want, (m, eps, rstd[m], want)
+
+
+def test_rmsnorm_output_from_library_products():
+    """y = bf16(fp32(fp32(x * rstd) * gamma)) with numpy's IEEE fp32 products
+    and torch's bf16 cast, elementwise (a shifted or transposed gamma index,
+    or a missing product, fails)."""
+    M, K = 16, 1024
+    x = synthetic.activations(M, K, seed=4, n_out=3)
+    gamma = bf16(np.random.default_rng(7).uniform(-2, 2, K).astype(np.float32))
+    y, rstd = oracle.rmsnorm_bf16(x, gamma, 1e-5)
+    t = (f32(x) * rstd[:, None]).astype(np.float32)
+    u = (t * f32(gamma)[None, :]).astype(np.float32)
+    assert np.array_equal(y, torch_bf16_bits(u))
+
+
+def test_rmsnorm_unit_mean_square():
+    """With gamma = 1 and eps = 0 the output has mean square 1 up to the bf16
+    rounding of each element (relative error <= 2^-8 each)."""
+    M, K = 32, 4096
+    x = synthetic.activations(M, K, seed=5, n_out=4)
+    y, _ = oracle.rmsnorm_bf16(x, bf16(np.ones(K)), 0.0)
+    ms = np.mean(f32(y).astype(np.float64) ** 2, axis=1)
+    assert np.all(np.abs(ms - 1.0) <= 2.0 ** -7), ms
+
+
+def test_rmsnorm_closed_forms():
+    """Rows of +-2^e: the mean square is 4^e, rstd = 2^-e exactly, y = +-gamma.
+    eps = 0: scaling x by a power of two leaves y unchanged bit for bit.
+    An all-zero row with eps > 0 gives signed-zero outputs."""
+    K = 256
+    gamma = bf16(np.random.default_rng(1).normal(0, 1, K).astype(np.float32))
+    signs = np.where(np.random.default_rng(2).random(K) < 0.5, -1.0, 1.0)
+    for e in (-20, -3, 0, 5, 30):
+        x = bf16((signs * 2.0 ** e)[None, :])
+        y, rstd = oracle.rmsnorm_bf16(x, gamma, 0.0)
+        assert rstd[0] == np.float32(2.0 ** -e)
+        want = np.where(signs < 0, gamma ^ np.uint16(0x8000), gamma)
+        assert np.array_equal(y[0], want)
+    x = synthetic.activations(8, K, seed=6, n_out=1)
+    y0, r0 = oracle.rmsnorm_bf16(x, gamma, 0.0)
+    for j in (-12, -1, 3, 40):
+        xs = bf16(f32(x) * np.float32(2.0 ** j))
+        assert np.array_equal(f32(xs), f32(x) * np.float32(2.0 ** j))   # exact scaling
+        yj, rj = oracle.rmsnorm_bf16(xs, gamma, 0.0)
+        assert np.array_equal(yj, y0)
+        assert np.array_equal(rj, r0 * np.float32(2.0 ** -j))
+    z = np.zeros((2, K), np.uint16)
+    z[1, ::3] = 0x8000                                          # -0 entries
+    y, rstd = oracle.rmsnorm_bf16(z, gamma, 1e-6)
+    assert np.all((y & 0x7FFF) == 0)
+    q, s, _ = oracle.rmsnorm_quant(z, gamma, 1e-6)
+    assert np.all(s == 0) and np.all((q & 0x7F) == 0)
+
+
+def test_rmsnorm_quant_is_quant_of_output():
+    """The fused result is quant_act of the BF16 RMSNorm output, and every
+    non-zero group reaches code magnitude 448."""
+    M, K = 8, 3584
+    x = synthetic.activations(M, K, seed=8, n_out=4)
+    gamma = bf16(np.random.default_rng(3).uniform(0.5, 1.5, K).astype(np.float32))
+    q, s, r = oracle.rmsnorm_quant(x, gamma, 1e-6)
+    y, r2 = oracle.rmsnorm_bf16(x, gamma, 1e-6)
+    q2, s2 = oracle.quant_act(y)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(r, r2)
+    mags = (q & 0x7F).reshape(M, K // G, G).max(axis=2)
+    assert np.all(mags == 0x7E)
+
+
+# ------------------------------------------------------------------- SwiGLU
+
+def exact_swiglu_bf16(gv: float, uv: float):
+    """bf16 of g*u/(1+exp(-g)) from 60-digit decimal arithmetic, and the
+    value's relative distance to the nearest bf16 rounding midpoint."""
+    getcontext().prec = 60
+    g, u = Decimal(gv), Decimal(uv)
+    v = g * u / (1 + (-g).exp())
+    q = Fraction(v)
+    return round_fraction(q, 8, -126), midpoint_distance(q, 8, -126)
+
+
+def swiglu_cases():
+    g = np.random.default_rng(11)
+    gate = np.concatenate([
+        g.normal(0, 1, 4000), g.normal(0, 1, 500) * 50, g.uniform(-20, 20, 500),
+        np.array([0.0, -0.0, 1.0, -1.0, 128.0, -128.0, 88.0, -88.0, 700.0, -700.0, 1e-30, -1e-30]),
+    ]).astype(np.float32)
+    up = np.concatenate([
+        g.normal(0, 1, 4000), g.normal(0, 1, 500), g.normal(0, 3, 500),
+        np.array([1.0, 1.0, -2.0, 3.0, 1.0, 1.0, -1.0, 1.0, 2.0, 1.0, 1.0, 1.0]),
+    ]).astype(np.float32)
+    n = gate.size - gate.size % G
+    return bf16(gate[:n]).reshape(-1, G), bf16(up[:n]).reshape(-1, G)
+
+
+def test_swiglu_matches_high_precision():
+    """Every element equals bf16 (nearest even) of the exact silu(g)*u from
+    60-digit decimal arithmetic, except where that value is within 2^-40 of a
+    rounding midpoint; those must be flagged as near ties."""
+    gb, ub = swiglu_cases()
+    h, near = oracle.swiglu_bf16(gb, ub)
+    gf, uf = f32(gb).ravel(), f32(ub).ravel()
+    hf = f32(h).ravel()
+    checked = 0
+    for i in range(gf.size):
+        want, dist = exact_swiglu_bf16(float(gf[i]), float(uf[i]))
+        if dist <= Fraction(1, 2 ** 40):
+            continue
+        assert not near.ravel()[i]
+        assert Fraction(float(hf[i])) == want, (i, gf[i], uf[i], hf[i], float(want))
+        checked += 1
+    assert checked > 0.99 * gf.size
+
+
+def test_swiglu_library_silu():
+    """Against torch's float64 silu times u, rounded to fp32 then bf16 by
+    library casts; the double rounding only differs from one rounding when the
+    fp32 value is exactly a bf16 midpoint, and such elements are skipped."""
+    M, F = 64, 1024
+    gb = synthetic.activations(M, F, seed=9, n_out=3)
+    ub = synthetic.activations(M, F, seed=10, n_out=0)
+    h, near = oracle.swiglu_bf16(gb, ub)
+    gt = torch.from_numpy(f32(gb).astype(np.float64))
+    v = (torch.nn.functional.silu(gt) * torch.from_numpy(f32(ub).astype(np.float64))).numpy()
+    v32 = v.astype(np.float32)
+    ok = (v32.view(np.uint32) & 0xFFFF) != 0x8000
+    assert np.array_equal(h[ok & ~near], torch_bf16_bits(v32)[ok & ~near])
+    assert near.sum() == 0
+
+
+def test_swiglu_special_values():
+    """silu(0) = 0 with the sign of g*u; large positive g passes g*u through;
+    large negative g underflows to a zero signed opposite to u."""
+    gb = bf16(np.array([[0.0, -0.0, 0.0, 128.0, 256.0, -128.0, -1000.0, -1000.0] * 16]))
+    ub = bf16(np.array([[3.0, 3.0, -3.0, 1.5, -0.375, 2.0, 5.0, -5.0] * 16]))
+    h, _ = oracle.swiglu_bf16(gb, ub)
+    row = h[0, :8]
+    assert list(row) == [0x0000, 0x8000, 0x8000, bf16(192.0)[()], bf16(-96.0)[()], 0x8000, 0x8000, 0x0000]
+
+
+def test_swiglu_quant_is_quant_of_output():
+    gb = synthetic.activations(16, 2048, seed=12, n_out=2)
+    ub = synthetic.activations(16, 2048, seed=13, n_out=0)
+    q, s, near = oracle.swiglu_quant(gb, ub)
+    h, near2 = oracle.swiglu_bf16(gb, ub)
+    q2, s2 = oracle.quant_act(h)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(near, near2)
