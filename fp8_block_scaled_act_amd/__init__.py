@@ -22,6 +22,7 @@ __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
     "fp8_gemm_fwd", "fp8_gemm_fwd_packed", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
+    "fp8_rmsnorm_quant", "fp8_swiglu_quant",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -55,6 +56,10 @@ _SYMBOLS = {
     "fp8_gemm_dgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_gemm_dgrad_t": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_gemm_wgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8_rmsnorm_quant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "fp8_swiglu_quant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
                            ctypes.c_int),
     "fp8lin_decode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
@@ -259,6 +264,56 @@ def fp8_linear_fwd(x, wq, sw, out=None, stream=None):
     _check(lib().fp8_linear_fwd(_ptr(x), _ptr(wq), _ptr(sw), M, N, K, _ptr(q), _ptr(s), _ptr(y), _stream(stream)),
            "fp8_linear_fwd")
     return y, q, s
+
+
+# ------------------------------------------------- producers fused with quant
+
+def fp8_rmsnorm_quant(x, gamma, eps: float = 1e-6, out=None, rstd: bool = True, stream=None):
+    """RMSNorm of x bf16 [M,K] with gamma bf16 [K], quantized 1x128 without
+    storing the BF16 output: returns (xq u8 [M,K], sx f32 [M,K/128], rstd f32 [M]
+    or None)."""
+    M, K = x.shape
+    _expect(x, "x", torch.bfloat16, (M, K))
+    _expect(gamma, "gamma", torch.bfloat16, (K,))
+    if out is None:
+        q, s = _empty((M, K), torch.uint8, x), _empty((M, K // GROUP), torch.float32, x)
+        r = _empty((M,), torch.float32, x) if rstd else None
+    else:
+        q, s, r = out
+    _expect(q, "xq", torch.uint8, (M, K))
+    _expect(s, "sx", torch.float32, (M, K // GROUP))
+    if r is not None:
+        _expect(r, "rstd", torch.float32, (M,))
+    _check(lib().fp8_rmsnorm_quant(_ptr(x), _ptr(gamma), M, K, float(eps), _ptr(q), _ptr(s), _ptr(r),
+                                   _stream(stream)), "fp8_rmsnorm_quant")
+    return q, s, r
+
+
+def fp8_swiglu_quant(gate, up, out=None, stream=None):
+    """silu(gate) * up of bf16 [M,F] operands, quantized 1x128 without storing
+    the BF16 product: returns (hq u8 [M,F], sh f32 [M,F/128]).  gate and up may
+    be row-strided views (e.g. the two halves of one [M,2F] tensor) with equal
+    row strides and unit column stride."""
+    if gate.shape != up.shape or gate.dim() != 2:
+        raise ValueError("gate and up must be 2-D tensors of one shape")
+    M, F = gate.shape
+    for t, name in ((gate, "gate"), (up, "up")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be torch.bfloat16" % name)
+        if t.numel() and not t.is_cuda:
+            raise ValueError("%s must be on the GPU" % name)
+        if M and F and t.stride(1) != 1:
+            raise ValueError("%s must have unit column stride" % name)
+    ld = gate.stride(0) if M > 1 else F
+    if M > 1 and up.stride(0) != ld:
+        raise ValueError("gate and up must have the same row stride")
+    q, s = out if out is not None else (_empty((M, F), torch.uint8, gate),
+                                        _empty((M, F // GROUP), torch.float32, gate))
+    _expect(q, "hq", torch.uint8, (M, F))
+    _expect(s, "sh", torch.float32, (M, F // GROUP))
+    _check(lib().fp8_swiglu_quant(_ptr(gate), _ptr(up), ld, M, F, _ptr(q), _ptr(s), _stream(stream)),
+           "fp8_swiglu_quant")
+    return q, s
 
 
 def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):

@@ -394,6 +394,59 @@ fp8lin_status fp8_linear_fwd(const void* x, const uint8_t* wq, const float* sw, 
     return end_launch();
 }
 
+fp8lin_status fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int64_t K, float eps,
+                                uint8_t* xq, float* sx, float* rstd, void* stream)
+{
+    if (M < 0 || K < 0 || K % kGroup != 0 || K > 16384 || (M + 3) / 4 > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 3.4028234663852886e38f)
+        return FP8LIN_ERR_ARG;
+    int64_t bx, bq, bs, br, bg;
+    if (!bytes_of(M, K, 2, &bx) || !bytes_of(M, K, 1, &bq) || !bytes_of(M, K / kGroup, 4, &bs) ||
+        !bytes_of(M, 1, 4, &br) || !bytes_of(K, 1, 2, &bg))
+        return FP8LIN_ERR_SHAPE;
+    if (bq == 0)
+        bg = br = 0;
+    const Buf in[] = {{x, bx}, {gamma, bg}};
+    const Buf out[] = {{xq, bq}, {sx, bs}, {rstd, rstd ? br : 0}};
+    fp8lin_status s = check_buffers(in, 2, out, 3);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bq == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_rmsnorm_quant(x, gamma, M, K, eps, xq, sx, rstd, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M, int64_t F,
+                               uint8_t* hq, float* sh, void* stream)
+{
+    if (M < 0 || F < 0 || F % kGroup != 0 || ld < F)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bq, bs, ng, span;
+    if (!bytes_of(M, F, 1, &bq) || !bytes_of(M, F / kGroup, 4, &bs) || !mul_ok(M, F / kGroup, &ng) ||
+        ng >= ((int64_t)1 << 32))
+        return FP8LIN_ERR_SHAPE;
+    if (bq == 0)
+        return FP8LIN_OK;
+    if (!mul_ok(M - 1, ld, &span) || span > INT64_MAX / 2 - F)
+        return FP8LIN_ERR_SHAPE;
+    const int64_t bin = (span + F) * 2;
+    if (ld % 8 != 0)
+        return FP8LIN_ERR_ALIGN;
+    const Buf in[] = {{gate, bin}, {up, bin}};
+    const Buf out[] = {{hq, bq}, {sh, bs}};
+    fp8lin_status s = check_buffers(in, 2, out, 2);
+    if (s != FP8LIN_OK)
+        return s;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_swiglu_quant(gate, up, ld, M, F, hq, sh, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t T,
                              int64_t N, int64_t K, void* dx, void* stream)
 {

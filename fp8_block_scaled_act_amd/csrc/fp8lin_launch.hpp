@@ -18,6 +18,12 @@ void launch_transpose_codes(const uint8_t* src, const float* s, int64_t R, int64
 void launch_encode_probe(const float* in, int64_t n, uint8_t* out, int method, hipStream_t st);
 void launch_decode_probe(const uint8_t* in, int64_t n, float* out, int method, hipStream_t st);
 
+// Producer operators fused with 1x128 quantization (K <= 16384 for RMSNorm).
+void launch_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int64_t K, float eps, uint8_t* q,
+                          float* s, float* rstd, hipStream_t st);
+void launch_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M, int64_t F, uint8_t* q,
+                         float* s, hipStream_t st);
+
 void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st);
 void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                      int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);

@@ -11,47 +11,6 @@
 
 namespace fp8lin {
 
-// Encoder / decoder used by the kernels: the gfx950 conversion instructions.
-// Checked on every fp32 input against the definition: v_cvt_pk_fp8_f32
-// rounds to nearest even into OCP E4M3FN (subnormals and ties included) for
-// |v| <= 464 and returns NaN above, so its inputs must stay within +-464; the
-// fast quotient never exceeds 448 (1 + 2^-23) and the slow one is clamped to
-// +-448.  v_cvt_pk_f32_fp8 decodes all 254 finite codes exactly.
-__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d)
-{
-    return e4m3_encode4_hw(a, b, c, d);
-}
-
-__device__ __forceinline__ void decode4(uint32_t w, float* v) { e4m3_decode4_hw(w, v); }
-
-// Quotients of n values with one group's scale, encoded 4 at a time.
-template <int N>
-__device__ __forceinline__ void quantize_n(const float* x, const GroupScale& g, uint32_t* out)
-{
-    float t[N];
-    if (g.fast) {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            t[i] = quotient_fast(x[i], g.s, g.r);
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            t[i] = quotient_slow(x[i], g.s);
-    }
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i)
-        out[i] = encode4(t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]);
-}
-
-__device__ __forceinline__ uint2 quantize8(uint4 v, const GroupScale& g)
-{
-    float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    uint32_t c[2];
-    quantize_n<8>(x, g, c);
-    return make_uint2(c[0], c[1]);
-}
-
 // ============================================================ 1x128 groups
 //
 // A [M,K] tensor with K % 128 == 0 is a flat sequence of 128-element groups

@@ -226,6 +226,51 @@ fp8lin_status fp8_linear_fwd(const void* x, const uint8_t* wq, const float* sw,
                              uint8_t* xq, float* sx, void* y, void* stream);
 
 /*
+ * RMSNorm fused with the 1x128 activation quantization of its output (the
+ * operator in front of the attention / MLP input projections).  Jet-RL
+ * summary, "Quantization scheme" (FP8 activations saved for the backward pass,
+ * produced fused with the previous operator) and "Implementation" (fused
+ * RMSNorm kernels).  The pages define no RMSNorm arithmetic; this call fixes
+ * it as:
+ *   ss[m]   = sum_k x[m,k]^2 in fp64, each 128-group summed as a balanced
+ *             binary tree and the group sums added in ascending order;
+ *   rstd[m] = fp32(1 / sqrt(ss[m] / K + eps)) (fp64 operations);
+ *   y[m,k]  = bf16(fp32(fp32(x[m,k] * rstd[m]) * gamma[k])), round to nearest even;
+ * and writes xq, sx = fp8_quant_act(y) without ever storing y.
+ *   x     : BF16 [M,K]              (input)
+ *   gamma : BF16 [K]                (input)
+ *   eps   : finite, >= 0
+ *   xq    : uint8 E4M3 [M,K]        (output)
+ *   sx    : float [M][K/128]        (output)
+ *   rstd  : float [M]               (output, may be NULL; kept for RMSNorm's backward)
+ * K % 128 == 0 and K <= 16384 (a row is held in registers), else
+ * FP8LIN_ERR_SHAPE; eps negative or not finite: FP8LIN_ERR_ARG.  M == 0 or
+ * K == 0 is an OK no-op.  A row with ss / K + eps == 0 (all zeros with
+ * eps == 0) is outside the contract.  Rows are independent.
+ */
+fp8lin_status fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int64_t K, float eps,
+                                uint8_t* xq, float* sx, float* rstd, void* stream);
+
+/*
+ * SwiGLU fused with the 1x128 activation quantization of its output (the
+ * input of the MLP down projection).  Jet-RL summary, "Quantization scheme"
+ * and "Implementation" (fused activation kernels).  The pages define no
+ * activation arithmetic; this call fixes it as
+ *   h[m,f] = bf16(silu(gate[m,f]) * up[m,f]),  silu(g) = g / (1 + exp(-g)),
+ * evaluated in fp64 and rounded once to BF16 (nearest even), and writes
+ * hq, sh = fp8_quant_act(h) without ever storing h.
+ *   gate, up : BF16, rows of F elements at row stride ld (elements), so they
+ *              may be two tensors or the two halves of one [M, 2F] tensor
+ *   hq       : uint8 E4M3 [M,F]     (output, dense)
+ *   sh       : float [M][F/128]     (output)
+ * F % 128 == 0, ld >= F, M * F / 128 < 2^32, else FP8LIN_ERR_SHAPE;
+ * ld % 8 != 0 (rows not 16-byte aligned): FP8LIN_ERR_ALIGN.  gate and up
+ * may overlap each other, not the outputs.  M == 0 or F == 0 is an OK no-op.
+ */
+fp8lin_status fp8_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M, int64_t F,
+                               uint8_t* hq, float* sh, void* stream);
+
+/*
  * DGrad GEMM (NN):  dX = dY W, contracted over W's row dimension N.
  * Jet-RL summary, "Quantization scheme": the backward DGrad GEMM runs in FP8.
  *   dX[t,k] = sum_g sdy[t][g] * sw[g][k/128] * sum_{n in g} dec(dyq[t,n]) dec(wq[n,k])

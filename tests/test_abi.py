@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(L):
     assert len(names) >= 11, names
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
               "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
-              "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
+              "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -175,6 +176,39 @@ def test_packed_decode_validation(L):
     assert L.fp8_gemm_fwd_packed(A, B, C, D, 4, 128, 256, C, s0) == ALIAS
     assert L.fp8_gemm_fwd_packed(None, None, None, None, 0, 128, 256, None, s0) == OK
     assert L.fp8_gemm_fwd_packed(A, B, C, D, 4, 128, 256, E, s0) == DEVICE
+
+
+@fake_ptrs
+def test_rmsnorm_quant_validation(L):
+    # x, gamma, M, K, eps, xq, sx, rstd
+    assert L.fp8_rmsnorm_quant(A, B, 4, 100, 1e-6, C, D, E, s0) == SHAPE       # K % 128
+    assert L.fp8_rmsnorm_quant(A, B, 4, 16512, 1e-6, C, D, E, s0) == SHAPE     # K > 16384
+    assert L.fp8_rmsnorm_quant(A, B, -1, 128, 1e-6, C, D, E, s0) == SHAPE
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, -1.0, C, D, E, s0) == ARG
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, float("nan"), C, D, E, s0) == ARG
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, float("inf"), C, D, E, s0) == ARG
+    assert L.fp8_rmsnorm_quant(A, None, 4, 128, 1e-6, C, D, E, s0) == NULL     # gamma
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, 1e-6, None, D, E, s0) == NULL
+    assert L.fp8_rmsnorm_quant(A, B + 2, 4, 128, 1e-6, C, D, E, s0) == ALIGN
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, 1e-6, C, D, A + 16, s0) == ALIAS   # rstd over x
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, 1e-6, B, D, E, s0) == ALIAS        # xq over gamma
+    assert L.fp8_rmsnorm_quant(None, None, 0, 128, 1e-6, None, None, None, s0) == OK
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, 1e-6, C, D, None, s0) == DEVICE   # rstd optional
+    assert L.fp8_rmsnorm_quant(A, B, 4, 128, 0.0, C, D, E, s0) == DEVICE
+
+
+@fake_ptrs
+def test_swiglu_quant_validation(L):
+    # gate, up, ld, M, F, hq, sh
+    assert L.fp8_swiglu_quant(A, B, 256, 4, 100, C, D, s0) == SHAPE           # F % 128
+    assert L.fp8_swiglu_quant(A, B, 128, 4, 256, C, D, s0) == SHAPE           # ld < F
+    assert L.fp8_swiglu_quant(A, B, 2 ** 40, 2 ** 40, 128, C, D, s0) == SHAPE   # groups >= 2^32
+    assert L.fp8_swiglu_quant(A, B, 260, 4, 256, C, D, s0) == ALIGN           # rows not 16-byte aligned
+    assert L.fp8_swiglu_quant(None, B, 256, 4, 256, C, D, s0) == NULL
+    assert L.fp8_swiglu_quant(A, B, 256, 4, 256, A + 1024, D, s0) == ALIAS    # hq inside gate's rows
+    assert L.fp8_swiglu_quant(A, A + 256, 512, 4, 256, C, D, s0) == DEVICE    # halves of one tensor
+    assert L.fp8_swiglu_quant(None, None, 256, 0, 256, None, None, s0) == OK
+    assert L.fp8_swiglu_quant(A, B, 256, 4, 256, C, D, s0) == DEVICE
 
 
 @fake_ptrs
