@@ -79,6 +79,7 @@ class Step:
         self.kernels = []
         self.rotate = 1
         self.gemm_flop = 0
+        self.step_bytes = 0        # producers: algorithmic bytes of the step
         self.config = {}
 
     def add(self, name, fn, kind, units):
@@ -134,6 +135,22 @@ def build_step(name, torch, fl, synthetic):
                      "weight_copies_rotated": st.rotate}
         if name == "decode":
             st.config["weight_layout"] = "decode layout (fp8_weight_pack), made with the weight quantization"
+    elif wl.kind == "producers":
+        T, F, K = wl.M, wl.N, wl.K
+        x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
+        gamma = bf16(synthetic.norm_weights(K, seed=0))
+        gu = bf16(synthetic.activations(T, 2 * F, seed=1, n_out=synthetic.n_outliers(2 * F)))
+        gate, up = gu[:, :F], gu[:, F:]
+        xq, sx, rstd = empty((T, K), u8), empty((T, K // G), f32), empty((T,), f32)
+        hq, sh = empty((T, F), u8), empty((T, F // G), f32)
+        st.add("rmsnorm_quant", lambda i: fl.fp8_rmsnorm_quant(x, gamma, 1e-6, out=(xq, sx, rstd)), "hbm",
+               act_quant_bytes(T, K) + 4 * T + 2 * K)
+        st.add("swiglu_quant", lambda i: fl.fp8_swiglu_quant(gate, up, out=(hq, sh)), "hbm",
+               2 * T * F * 2 + T * F + T * (F // G) * 4)
+        st.dominant = "swiglu_quant"
+        st.step_bytes = sum(k[3] for k in st.kernels)
+        st.config = {"workload": wl.doc, "T": T, "K": K, "F": F, "eps": 1e-6,
+                     "outlier_columns": wl.n_out}
     else:
         T, N, K = wl.M, wl.N, wl.K
         dy = bf16(synthetic.grad_out(T, N, seed=0))
@@ -205,6 +222,7 @@ def time_graph(torch, g, reps):
 def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
     """The oracle, as it stands, on a bounded sample of the workload: the
     sampled step is repeated until at least min_seconds of CPU time."""
+    import numpy as np
     import oracle
     wl = synthetic.WORKLOADS[name]
     if wl.kind == "forward":
@@ -219,6 +237,31 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
             oracle.gemm_fwd(xq, sx, wq, sw)
         what = ("%d of %d rows of X per repetition: oracle 1x128 quantization + fp64 GEMM against "
                 "the full W (W quantized once, outside the timing)" % (rows, M))
+    elif wl.kind == "producers":
+        T, F, K = wl.M, wl.N, wl.K
+        rows = 1024
+        max_reps = 10 ** 6
+        x = synthetic.activations(T, K, seed=0, n_out=wl.n_out)[:rows]
+        gamma = synthetic.norm_weights(K, seed=0)
+        gu = synthetic.activations(T, 2 * F, seed=1, n_out=synthetic.n_outliers(2 * F))[:rows]
+        gate, up = np.ascontiguousarray(gu[:, :F]), np.ascontiguousarray(gu[:, F:])
+        del gu
+
+        def work():
+            oracle.rmsnorm_quant(x, gamma, 1e-6)
+            oracle.swiglu_quant(gate, up)
+        nbytes = act_quant_bytes(rows, K) + 4 * rows + 2 * K + 2 * rows * F * 2 + rows * F + rows * (F // G) * 4
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            work()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds or reps >= max_reps:
+                break
+        return {"value": nbytes * reps / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": "%d of %d token rows per repetition: oracle RMSNorm + 1x128 quantization of X rows and "
+                          "SwiGLU + 1x128 quantization of gate/up rows; %d repetitions" % (rows, T, reps),
+                "seconds": round(dt, 2)}
     else:
         T, N, K = wl.M, wl.N, wl.K
         rows = 8
@@ -254,6 +297,18 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
 # The ingest step writes profiles/traffic.json (bytes per launch, scaled by
 # the copy's calibration factor, with the kernel-source hash it belongs to).
 
+KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes from
+    "quant_act": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "quant_weight": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "quant_transpose_dual_dY": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "quant_transpose_fp8_X": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_fwd": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_dgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_wgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "rmsnorm_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
+    "swiglu_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
+}
+
 CALIB_BYTES = 1 << 30
 PROFILE_REPS = 5
 KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
@@ -264,6 +319,8 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "gemm_fwd": "gemm_",
     "gemm_dgrad": "Mode)0",     # the backward step runs DGrad as the NT GEMM on W^T
     "gemm_wgrad": "Mode)2",
+    "rmsnorm_quant": "rmsnorm_quant_kernel",
+    "swiglu_quant": "swiglu_quant_kernel",
 }
 
 
@@ -305,7 +362,6 @@ def ingest_pmc(name, fetch_csv, write_csv, torch, fl, synthetic):
     factor_f = CALIB_BYTES / (f_copy * 1024.0)
     factor_w = CALIB_BYTES / (w_copy * 1024.0)
     st = build_step(name, torch, fl, synthetic)
-    sha = source_hash("gemm_kernels.hip", "quant_kernels.hip", "fp8lin_device.hpp")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     for kname, _, kind, units in st.kernels:
@@ -320,7 +376,7 @@ def ingest_pmc(name, fetch_csv, write_csv, torch, fl, synthetic):
             "calibration": {"copy_bytes": CALIB_BYTES, "fetch_factor": round(factor_f, 4),
                             "write_factor": round(factor_w, 4)},
             "algorithmic_bytes": units if kind == "hbm" else None,
-            "source_sha": sha,
+            "source_sha": source_hash(*KERNEL_SOURCES[kname]),
         }
         log("[bench] %s/%s: %.1f MB per launch (fetch %.1f MiB, write %.1f MiB raw)" %
             (name, kname, b / 1e6, f / 1024, w / 1024))
@@ -336,7 +392,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny", "producers"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-eager", action="store_true",
                     help="run each kernel of the step eagerly (for rocprofv3 counter passes) and exit")
@@ -379,8 +435,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / steps
-    value = st.gemm_flop / (ms_per_step * 1e-3) / 1e12
+    if st.gemm_flop:
+        value, value_unit = st.gemm_flop / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+    else:
+        value, value_unit = st.step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
 
+    log("[bench] step: %.2f us, %.1f %s" % (ms_per_step * 1e3, value, value_unit))
     log("[bench] per-kernel timing")
     kernels = {}
     reps = max(4, min(200, steps // R))
@@ -410,19 +470,19 @@ def main():
     traffic_file = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(traffic_file):
         rec = json.load(open(traffic_file)).get("%s/%s" % (args.workload, dom))
-        if rec and rec.get("source_sha") == source_hash("gemm_kernels.hip", "quant_kernels.hip",
-                                                         "fp8lin_device.hpp"):
+        if rec and rec.get("source_sha") == source_hash(*KERNEL_SOURCES[dom]):
             roofline["traffic"] = rec["bytes_per_launch"]
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         cpu = cpu_baseline(args.workload, synthetic)
-        log("[bench]  oracle: %.6f TFLOP/s in %.1f s on %d threads" % (cpu["value"], cpu["seconds"], cpu["cores"]))
+        log("[bench]  oracle: %.6f %s in %.1f s on %d threads" % (cpu["value"], cpu["unit"], cpu["seconds"],
+                                                                 cpu["cores"]))
 
     line = {
         "metric": "FP8 block-scaled GEMM TFLOP/s (% of FP8 MFMA peak); quant GB/s (% HBM)",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "value": round(value, 2), "unit": value_unit, "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
         "config": st.config, "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,

@@ -13,8 +13,10 @@
 //             fp64 sum of x^2, is summed as a balanced binary tree over each
 //             128-group and the group sums are added in ascending order
 //             (a fixed order, so the result does not depend on the launch);
-//   SwiGLU:   h = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g)), evaluated
-//             in fp64 and rounded once to BF16.
+//   SwiGLU:   h = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g)), the
+//             fp64 evaluation rounded once to BF16 (reached through an fp32
+//             evaluation with a proven error bound, fp64 where that bound
+//             cannot decide the rounding).
 #include "fp8lin_device.hpp"
 #include "fp8lin_launch.hpp"
 
@@ -82,12 +84,47 @@ __device__ __forceinline__ uint2 quantize_group16(uint4 y, float& scale)
 // ==================================================== RMSNorm -> FP8 1x128
 //
 // One wave per row: lane l holds elements [512 i + 8 l, +8) of pass i in
-// registers (NV passes, K <= 512 NV), so the row is read from HBM once.  The
-// squares are summed in fp64 in the stated order: 8 in-lane values as a
-// tree, then 16 lanes by xor exchange (a balanced tree over the 128-group,
-// identical in every lane because fp64 addition is commutative), then the
-// group sums in ascending order through lane reads.  Gamma (shared by every
-// row) is read in the second pass from the cache.
+// registers (NV passes, 512 (NV - 1) < K <= 512 NV for K <= 8192), so the row
+// is read from HBM once.  Lanes past the end of the row load a valid address
+// (the row's first chunk) and zero it, so no load sits behind a branch and all
+// of a row's loads, and gamma's, are in flight together.  The squares are
+// summed in fp64 in the stated order: the lane's 8 values as a tree, then 16
+// lanes by DPP exchanges (quad xor 1, quad xor 2, half-row mirror, row mirror:
+// after each step every lane of a block holds the block's sum, so each step
+// adds two sibling subtrees of the balanced tree over the 128-group), then the
+// group sums in ascending order through lane reads.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const long long b = __double_as_longlong(v);
+    const uint32_t lo = dpp<CTRL>((uint32_t)(b & 0xFFFFFFFFll));
+    const uint32_t hi = dpp<CTRL>((uint32_t)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double sum_over_16_lanes(double t)
+{
+    t = t + dpp_f64<kDppQuadXor1>(t);
+    t = t + dpp_f64<kDppQuadXor2>(t);
+    t = t + dpp_f64<kDppRowHalfMirror>(t);
+    t = t + dpp_f64<kDppRowMirror>(t);
+    return t;
+}
+
+__device__ __forceinline__ double tree_sum_sq8(uint4 v)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    double sq[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const double lo = (double)bf16_lo(w[j]);
+        const double hi = (double)bf16_hi(w[j]);
+        sq[2 * j] = lo * lo;
+        sq[2 * j + 1] = hi * hi;
+    }
+    return ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+}
+
 template <int NV>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ gamma,
@@ -102,51 +139,49 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
         return;                                             // wave-uniform
     const int G = K >> 7;
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
-    uint4 v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        v[i] = (512 * i + 8 * lane < K) ? load_nt(xr + 64 * i + lane) : make_uint4(0, 0, 0, 0);
-
-    double ss = 0.0;
+    const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+    // Rows up to 8192 wide also hold gamma in registers from the start; wider
+    // rows read it in the second pass (register budget).
+    constexpr bool kGammaFirst = NV <= 16;
+    uint4 v[NV], gw[kGammaFirst ? NV : 1];
+    bool live[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        if (512 * i >= K)
-            continue;                                       // wave-uniform
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        double sq[8];
+        live[i] = 512 * i + 8 * lane < K;                   // uniform over each 16-lane group
+        const int c = live[i] ? 64 * i + lane : lane & 15;
+        v[i] = load_nt(xr + c);
+        if (kGammaFirst)
+            gw[i] = gr[c];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        if (!live[i])
+            v[i] = make_uint4(0, 0, 0, 0);
+
+    double t[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        t[i] = sum_over_16_lanes(tree_sum_sq8(v[i]));
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const double lo = (double)bf16_lo(w[j]);
-            const double hi = (double)bf16_hi(w[j]);
-            sq[2 * j] = lo * lo;
-            sq[2 * j + 1] = hi * hi;
+            const double gsum = readlane_f64(t[i], 16 * j);
+            ss = ss + (4 * i + j < G ? gsum : 0.0);          // adding +0 leaves ss unchanged
         }
-        double t = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
-        t = t + shfl_xor_f64(t, 1);
-        t = t + shfl_xor_f64(t, 2);
-        t = t + shfl_xor_f64(t, 4);
-        t = t + shfl_xor_f64(t, 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (4 * i + j < G)                              // wave-uniform
-                ss = ss + readlane_f64(t, 16 * j);
-    }
     const double r = 1.0 / __builtin_sqrt(ss / (double)K + (double)eps);
     const float rs = (float)r;
     if (rstd_out != nullptr && lane == 0)
         rstd_out[row] = rs;
 
-    const uint4* gr = reinterpret_cast<const uint4*>(gamma);
     uint2* qr = reinterpret_cast<uint2*>(q + row * K);
     float* sr = s + row * G;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        if (512 * i >= K)
-            continue;                                       // wave-uniform
-        const bool live = 512 * i + 8 * lane < K;           // uniform over each 16-lane group
-        const uint4 gw = live ? gr[64 * i + lane] : make_uint4(0, 0, 0, 0);
+        const uint4 g4 = kGammaFirst ? gw[i] : gr[live[i] ? 64 * i + lane : lane & 15];
         const uint32_t xw[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w};
+        const uint32_t gg[4] = {g4.x, g4.y, g4.z, g4.w};
         uint32_t yw[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -156,7 +191,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
         }
         float scale;
         const uint2 c = quantize_group16(make_uint4(yw[0], yw[1], yw[2], yw[3]), scale);
-        if (live) {
+        if (live[i]) {
             qr[64 * i + lane] = c;
             if ((lane & 15) == 0)
                 sr[4 * i + (lane >> 4)] = scale;
@@ -166,6 +201,68 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
 
 // ===================================================== SwiGLU -> FP8 1x128
 //
+// The reference evaluation is fp64: (g / (1 + exp(-g))) * u, rounded once to
+// BF16; its error (a few fp64 ulps) cannot move the rounding except within
+// 2^-44 of a BF16 midpoint.  The kernel first evaluates in fp32:
+//   e = v_exp_f32(g * fl(-log2 e)),  v = (g * v_rcp_f32(1 + e)) * u.
+// For |g| < 64 its relative error is at most
+//   |g| 2^-23 (the rounded exponent argument, times ln 2)
+//   + 2 ulp (exp) + 1 ulp (rcp) + 2 half-ulp roundings (add, products)
+//   <= 137 * 2^-24, i.e. at most ~140 ulps of v;
+// so when v's fp32 bits lie more than 512 ulps from a BF16 midpoint (low 16
+// bits outside [0x7E00, 0x8200]) the exact value rounds to the same BF16 as v.
+// Every other element, and every |g| >= 64, is evaluated again in fp64 (about
+// 1.6% of elements; the wave loops over each lane's flagged elements).
+__device__ __forceinline__ uint32_t swiglu_bf16_f64(float g, float u)
+{
+    const double gd = g, ud = u;
+    return f64_to_bf16_rne((gd / (1.0 + exp(-gd))) * ud);
+}
+
+__device__ __forceinline__ uint32_t swiglu_bf16_f32(float g, float u, bool& redo)
+{
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    const float v = (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
+    const uint32_t b = __float_as_uint(v);
+    redo = ((b - 0x7E00u) & 0xFFFFu) <= 0x400u || __builtin_fabsf(g) >= 64.0f;
+    return f32_to_bf16_rne(v);
+}
+
+// The 8 BF16 results of one lane's 16-byte chunks of gate and up.
+__device__ __forceinline__ uint4 swiglu8(uint4 gv, uint4 uv)
+{
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t hw[4];
+    uint32_t need = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bool r0, r1;
+        const uint32_t h0 = swiglu_bf16_f32(bf16_lo(gw[j]), bf16_lo(uw[j]), r0);
+        const uint32_t h1 = swiglu_bf16_f32(bf16_hi(gw[j]), bf16_hi(uw[j]), r1);
+        hw[j] = h0 | (h1 << 16);
+        need |= (r0 ? 1u << (2 * j) : 0u) | (r1 ? 2u << (2 * j) : 0u);
+    }
+    while (need != 0) {                                     // divergent: flagged elements only
+        const int k = __builtin_ctz(need);
+        need &= need - 1;
+        uint32_t gsel = 0, usel = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((k >> 1) == j) {
+                gsel = gw[j];
+                usel = uw[j];
+            }
+        const bool hi = k & 1;
+        const uint32_t hb = swiglu_bf16_f64(hi ? bf16_hi(gsel) : bf16_lo(gsel), hi ? bf16_hi(usel) : bf16_lo(usel));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((k >> 1) == j)
+                hw[j] = hi ? ((hw[j] & 0xFFFFu) | (hb << 16)) : ((hw[j] & 0xFFFF0000u) | hb);
+    }
+    return make_uint4(hw[0], hw[1], hw[2], hw[3]);
+}
+
 // Elementwise with 1x128 groups: 16 lanes per group, 8 values per lane, a
 // wave covers 4 groups per step and keeps UNROLL steps of loads in flight.
 // Group gi is row gi / GF, columns [128 (gi % GF), +128) of gate and up (row
@@ -187,32 +284,18 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
 #pragma unroll
         for (int k = 0; k < UNROLL; ++k) {
             const uint32_t gi = base + k * 4 + slot;
-            if (gi < ngroups) {
-                const uint32_t m = gi / GF, j = gi - m * GF;
-                const int64_t off = (int64_t)m * ld + (int64_t)j * kGroup + sub * 8;
-                gv[k] = load_nt(gate + off);
-                uv[k] = load_nt(up + off);
-            } else {
-                gv[k] = make_uint4(0, 0, 0, 0);
-                uv[k] = make_uint4(0, 0, 0, 0);
-            }
+            // past the end: re-read group 0 (always valid) and discard the result
+            const uint32_t gc = gi < ngroups ? gi : 0u;
+            const uint32_t m = gc / GF, j = gc - m * GF;
+            const int64_t off = (int64_t)m * ld + (int64_t)j * kGroup + sub * 8;
+            gv[k] = load_nt(gate + off);
+            uv[k] = load_nt(up + off);
         }
 #pragma unroll
         for (int k = 0; k < UNROLL; ++k) {
             const uint32_t gi = base + k * 4 + slot;
-            const uint32_t gw[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
-            const uint32_t uw[4] = {uv[k].x, uv[k].y, uv[k].z, uv[k].w};
-            uint32_t hw[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const double g0 = (double)bf16_lo(gw[j]), g1 = (double)bf16_hi(gw[j]);
-                const double u0 = (double)bf16_lo(uw[j]), u1 = (double)bf16_hi(uw[j]);
-                const double h0 = (g0 / (1.0 + exp(-g0))) * u0;
-                const double h1 = (g1 / (1.0 + exp(-g1))) * u1;
-                hw[j] = f64_to_bf16_rne(h0) | (f64_to_bf16_rne(h1) << 16);
-            }
             float scale;
-            const uint2 c = quantize_group16(make_uint4(hw[0], hw[1], hw[2], hw[3]), scale);
+            const uint2 c = quantize_group16(swiglu8(gv[k], uv[k]), scale);
             if (gi < ngroups) {
                 q[(int64_t)gi * 16 + sub] = c;
                 if (sub == 0)
@@ -224,25 +307,32 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
 
 // ================================================================ launchers
 
+template <int NV>
+static void rmsnorm_launch(const uint16_t* xp, const uint16_t* gp, int64_t M, int K, float eps, uint8_t* q,
+                           float* s, float* rstd, hipStream_t st)
+{
+    rmsnorm_quant_kernel<NV><<<(unsigned)((M + 3) / 4), 256, 0, st>>>(xp, gp, M, K, eps, q, s, rstd);
+}
+
 void launch_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int64_t K, float eps, uint8_t* q,
                           float* s, float* rstd, hipStream_t st)
 {
+    // As many register passes as the row needs (K <= 8192); wider rows (to
+    // 16384) take 32 passes, the surplus ones masked.
+    using Fn = void (*)(const uint16_t*, const uint16_t*, int64_t, int, float, uint8_t*, float*, float*,
+                        hipStream_t);
+    static constexpr Fn by_passes[17] = {
+        nullptr, rmsnorm_launch<1>, rmsnorm_launch<2>, rmsnorm_launch<3>, rmsnorm_launch<4>,
+        rmsnorm_launch<5>, rmsnorm_launch<6>, rmsnorm_launch<7>, rmsnorm_launch<8>, rmsnorm_launch<9>,
+        rmsnorm_launch<10>, rmsnorm_launch<11>, rmsnorm_launch<12>, rmsnorm_launch<13>, rmsnorm_launch<14>,
+        rmsnorm_launch<15>, rmsnorm_launch<16>};
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const uint16_t* gp = static_cast<const uint16_t*>(gamma);
-    const unsigned blocks = (unsigned)((M + 3) / 4);
-    const int k = (int)K;
-    if (K <= 512)
-        rmsnorm_quant_kernel<1><<<blocks, 256, 0, st>>>(xp, gp, M, k, eps, q, s, rstd);
-    else if (K <= 1024)
-        rmsnorm_quant_kernel<2><<<blocks, 256, 0, st>>>(xp, gp, M, k, eps, q, s, rstd);
-    else if (K <= 2048)
-        rmsnorm_quant_kernel<4><<<blocks, 256, 0, st>>>(xp, gp, M, k, eps, q, s, rstd);
-    else if (K <= 4096)
-        rmsnorm_quant_kernel<8><<<blocks, 256, 0, st>>>(xp, gp, M, k, eps, q, s, rstd);
-    else if (K <= 8192)
-        rmsnorm_quant_kernel<16><<<blocks, 256, 0, st>>>(xp, gp, M, k, eps, q, s, rstd);
+    const int64_t passes = (K + 511) / 512;
+    if (passes <= 16)
+        by_passes[passes](xp, gp, M, (int)K, eps, q, s, rstd, st);
     else
-        rmsnorm_quant_kernel<32><<<blocks, 256, 0, st>>>(xp, gp, M, k, eps, q, s, rstd);
+        rmsnorm_launch<32>(xp, gp, M, (int)K, eps, q, s, rstd, st);
 }
 
 void launch_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M, int64_t F, uint8_t* q,

@@ -19,7 +19,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TID_X, TID_W, TID_DY, TID_OUTLIER = 1, 2, 3, 4
+TID_X, TID_W, TID_DY, TID_OUTLIER, TID_NORM = 1, 2, 3, 4, 5
 
 
 def rng(seed: int, tid: int) -> np.random.Generator:
@@ -70,6 +70,13 @@ def weights(N: int, K: int, seed: int = 0, sigma: float = 0.02) -> np.ndarray:
     return gaussian_bf16((N, K), sigma, seed, TID_W)
 
 
+def norm_weights(K: int, seed: int = 0, sigma: float = 0.1) -> np.ndarray:
+    """RMSNorm gain gamma ~ 1 + N(0, 0.1) [K] as bf16 bits."""
+    g = rng(seed, TID_NORM)
+    a = np.float32(1.0) + g.standard_normal(size=(K,), dtype=np.float32) * np.float32(sigma)
+    return f32_to_bf16_bits(a)
+
+
 def grad_out(T: int, N: int, seed: int = 0, sigma: float = 1e-3) -> np.ndarray:
     """dY ~ N(0, 1e-3) [T,N] as bf16 bits."""
     return gaussian_bf16((T, N), sigma, seed, TID_DY)
@@ -90,7 +97,7 @@ def random_scales(shape, seed: int, tid: int, lo: float = 1e-3, hi: float = 2e-2
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str          # "forward" or "backward"
+    kind: str          # "forward", "backward" or "producers"
     M: int             # tokens (T for backward)
     N: int
     K: int
@@ -109,4 +116,7 @@ WORKLOADS = {
                          "8B-shaped MLP backward, dY[8192,14336] X[8192,4096] W[14336,4096]"),
     "large": Workload("large", "forward", 16384, 27648, 5120, n_outliers(5120),
                       "32B-shaped MLP forward, X[16384,5120] W[27648,5120]"),
+    "producers": Workload("producers", "producers", 8192, 14336, 4096, n_outliers(4096),
+                          "8B-shaped producers fused with 1x128 quantization: RMSNorm of X[8192,4096], "
+                          "SwiGLU of the gate/up halves of one [8192,2x14336] projection output"),
 }
