@@ -135,6 +135,43 @@ def build_step(name, torch, fl, synthetic):
                      "weight_copies_rotated": st.rotate}
         if name == "decode":
             st.config["weight_layout"] = "decode layout (fp8_weight_pack), made with the weight quantization"
+    elif wl.kind == "mlp":
+        T, F, K = wl.M, wl.N, wl.K
+        x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
+        gamma = bf16(synthetic.norm_weights(K, seed=0))
+        wgu_b = bf16(synthetic.weights(2 * F, K, seed=0))
+        wd_b = bf16(synthetic.weights(K, F, seed=1))
+        decode = T <= 64
+        per_copy = 3 * F * K
+        st.rotate = max(3, -(-2 * MALL_BYTES // per_copy)) if decode else 1
+        ws = []
+        for r in range(st.rotate):
+            wgu, sgu = fl.fp8_quant_weight(wgu_b)
+            wd, sd = fl.fp8_quant_weight(wd_b)
+            if decode:                              # decode layout, made with the weight quantization
+                wgu, wd = fl.fp8_weight_pack(wgu), fl.fp8_weight_pack(wd)
+            ws.append((wgu, sgu, wd, sd))
+        torch.cuda.synchronize()
+        del wgu_b, wd_b
+        xq, sx, rstd = empty((T, K), u8), empty((T, K // G), f32), empty((T,), f32)
+        gu = empty((T, 2 * F), bf)
+        hq, sh = empty((T, F), u8), empty((T, F // G), f32)
+        y = empty((T, K), bf)
+        gemm = fl.fp8_gemm_fwd_packed if decode else fl.fp8_gemm_fwd
+        kind = "hbm" if decode else "mfma"
+        st.add("rmsnorm_quant", lambda i: fl.fp8_rmsnorm_quant(x, gamma, 1e-6, out=(xq, sx, rstd)), "hbm",
+               act_quant_bytes(T, K) + 4 * T + 2 * K)
+        st.add("gemm_gate_up", lambda i: gemm(xq, sx, ws[i % st.rotate][0], ws[i % st.rotate][1], out=gu), kind,
+               gemm_bytes(T, 2 * F, K, (2 * F // G) * (K // G)) if decode else 2 * T * 2 * F * K)
+        st.add("swiglu_quant", lambda i: fl.fp8_swiglu_quant(gu[:, :F], gu[:, F:], out=(hq, sh)), "hbm",
+               2 * T * F * 2 + T * F + T * (F // G) * 4)
+        st.add("gemm_down", lambda i: gemm(hq, sh, ws[i % st.rotate][2], ws[i % st.rotate][3], out=y), kind,
+               gemm_bytes(T, K, F, (K // G) * (F // G)) if decode else 2 * T * K * F)
+        st.dominant = "gemm_gate_up"
+        st.gemm_flop = 6 * T * K * F
+        st.config = {"workload": wl.doc, "T": T, "K": K, "F": F, "eps": 1e-6, "outlier_columns": wl.n_out,
+                     "weight_copies_rotated": st.rotate,
+                     "same_kernels_as": "fp8_mlp_fwd (one call; bit-identical outputs)"}
     elif wl.kind == "producers":
         T, F, K = wl.M, wl.N, wl.K
         x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
@@ -237,6 +274,32 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
             oracle.gemm_fwd(xq, sx, wq, sw)
         what = ("%d of %d rows of X per repetition: oracle 1x128 quantization + fp64 GEMM against "
                 "the full W (W quantized once, outside the timing)" % (rows, M))
+    elif wl.kind == "mlp":
+        T, F, K = wl.M, wl.N, wl.K
+        rows = min(T, 8)
+        x = synthetic.activations(T, K, seed=0, n_out=wl.n_out)[:rows]
+        gamma = synthetic.norm_weights(K, seed=0)
+        owgu, osgu = oracle.quant_weight(synthetic.weights(2 * F, K, seed=0))
+        owd, osd = oracle.quant_weight(synthetic.weights(K, F, seed=1))
+
+        def work():
+            xq, sx, _ = oracle.rmsnorm_quant(x, gamma, 1e-6)
+            gu = oracle.f64_to_bf16(oracle.gemm_fwd(xq, sx, owgu, osgu))
+            hq, sh, _ = oracle.swiglu_quant(np.ascontiguousarray(gu[:, :F]), np.ascontiguousarray(gu[:, F:]))
+            oracle.gemm_fwd(hq, sh, owd, osd)
+        flop = 6 * rows * K * F
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            work()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds or reps >= max_reps:
+                break
+        return {"value": flop * reps / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": "%d of %d token rows per repetition through the oracle block: RMSNorm + quantization, "
+                          "fp64 gate/up GEMM, bf16 rounding, SwiGLU + quantization, fp64 down GEMM (weights "
+                          "quantized once, outside the timing); %d repetitions" % (rows, T, reps),
+                "seconds": round(dt, 2)}
     elif wl.kind == "producers":
         T, F, K = wl.M, wl.N, wl.K
         rows = 1024
@@ -305,11 +368,13 @@ KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes f
     "gemm_fwd": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_dgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_wgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "rmsnorm_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
 }
 
-CALIB_BYTES = 1 << 30
+CALIB_BYTES = 4 << 30
 PROFILE_REPS = 5
 KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "quant_act": "quant_rowgroup_kernel",
@@ -319,6 +384,8 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "gemm_fwd": "gemm_",
     "gemm_dgrad": "Mode)0",     # the backward step runs DGrad as the NT GEMM on W^T
     "gemm_wgrad": "Mode)2",
+    "gemm_gate_up": None,       # same kernel as gemm_down: counters cannot tell them apart
+    "gemm_down": None,
     "rmsnorm_quant": "rmsnorm_quant_kernel",
     "swiglu_quant": "swiglu_quant_kernel",
 }
@@ -358,7 +425,13 @@ def ingest_pmc(name, fetch_csv, write_csv, torch, fl, synthetic):
         return sum(xs) / len(xs) if xs else None
 
     copy_pred = lambda k: "elementwise" in k or "copy" in k.lower()
-    f_copy, w_copy = avg_kib(fetch, copy_pred), avg_kib(write, copy_pred)
+
+    def calib_kib(table):
+        # the calibration copies are the largest copy dispatches (input uploads
+        # of the step are small copies too)
+        xs = sorted((v for k, vs in table.items() if copy_pred(k) for v in vs), reverse=True)[:PROFILE_REPS]
+        return sum(xs) / len(xs)
+    f_copy, w_copy = calib_kib(fetch), calib_kib(write)
     factor_f = CALIB_BYTES / (f_copy * 1024.0)
     factor_w = CALIB_BYTES / (w_copy * 1024.0)
     st = build_step(name, torch, fl, synthetic)
@@ -366,6 +439,8 @@ def ingest_pmc(name, fetch_csv, write_csv, torch, fl, synthetic):
     data = json.load(open(path)) if os.path.exists(path) else {}
     for kname, _, kind, units in st.kernels:
         sym = KERNEL_SYMBOLS[kname]
+        if sym is None:
+            continue
         pred = lambda k, sym=sym: sym in k and not copy_pred(k)
         f, w = avg_kib(fetch, pred), avg_kib(write, pred)
         if f is None or w is None:
@@ -392,7 +467,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny", "producers"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny", "producers", "mlp", "mlp_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-eager", action="store_true",
                     help="run each kernel of the step eagerly (for rocprofv3 counter passes) and exit")

@@ -22,7 +22,7 @@ __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
     "fp8_gemm_fwd", "fp8_gemm_fwd_packed", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
-    "fp8_rmsnorm_quant", "fp8_swiglu_quant",
+    "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_mlp_fwd",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -60,6 +60,8 @@ _SYMBOLS = {
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "fp8_swiglu_quant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "fp8_mlp_fwd": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float] + [ctypes.c_void_p] * 4 +
+                    [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 8, ctypes.c_int),
     "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
                            ctypes.c_int),
     "fp8lin_decode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
@@ -314,6 +316,43 @@ def fp8_swiglu_quant(gate, up, out=None, stream=None):
     _check(lib().fp8_swiglu_quant(_ptr(gate), _ptr(up), ld, M, F, _ptr(q), _ptr(s), _stream(stream)),
            "fp8_swiglu_quant")
     return q, s
+
+
+def fp8_mlp_fwd(x, gamma, wgu, sgu, wdown, sdown, eps: float = 1e-6, out=None, rstd: bool = True, stream=None):
+    """Forward pass of an FP8 MLP block: RMSNorm -> gate/up GEMM -> SwiGLU -> down GEMM.
+
+    x bf16 [T,K], gamma bf16 [K], wgu/sgu the 128x128 quantization of the fused
+    [gate; up] weight [2F,K], wdown/sdown that of the down weight [K,F].
+    Returns dict(y, xq, sx, rstd, gu, hq, sh): the output and what the backward
+    pass keeps (FP8 inputs of both linear layers, rstd, and the BF16 gate/up
+    output)."""
+    T, K = x.shape
+    F2 = wgu.shape[0]
+    F = F2 // 2
+    _expect(x, "x", torch.bfloat16, (T, K))
+    _expect(gamma, "gamma", torch.bfloat16, (K,))
+    _expect(wgu, "wgu", torch.uint8, (F2, K))
+    _expect(sgu, "sgu", torch.float32, (F2 // GROUP, K // GROUP))
+    _expect(wdown, "wdown", torch.uint8, (K, F))
+    _expect(sdown, "sdown", torch.float32, (K // GROUP, F // GROUP))
+    if out is None:
+        out = {"y": _empty((T, K), torch.bfloat16, x), "xq": _empty((T, K), torch.uint8, x),
+               "sx": _empty((T, K // GROUP), torch.float32, x),
+               "rstd": _empty((T,), torch.float32, x) if rstd else None,
+               "gu": _empty((T, F2), torch.bfloat16, x), "hq": _empty((T, F), torch.uint8, x),
+               "sh": _empty((T, F // GROUP), torch.float32, x)}
+    _expect(out["y"], "y", torch.bfloat16, (T, K))
+    _expect(out["xq"], "xq", torch.uint8, (T, K))
+    _expect(out["sx"], "sx", torch.float32, (T, K // GROUP))
+    if out["rstd"] is not None:
+        _expect(out["rstd"], "rstd", torch.float32, (T,))
+    _expect(out["gu"], "gu", torch.bfloat16, (T, F2))
+    _expect(out["hq"], "hq", torch.uint8, (T, F))
+    _expect(out["sh"], "sh", torch.float32, (T, F // GROUP))
+    _check(lib().fp8_mlp_fwd(_ptr(x), _ptr(gamma), float(eps), _ptr(wgu), _ptr(sgu), _ptr(wdown), _ptr(sdown),
+                             T, K, F, _ptr(out["xq"]), _ptr(out["sx"]), _ptr(out["rstd"]), _ptr(out["gu"]),
+                             _ptr(out["hq"]), _ptr(out["sh"]), _ptr(out["y"]), _stream(stream)), "fp8_mlp_fwd")
+    return out
 
 
 def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):

@@ -447,6 +447,53 @@ fp8lin_status fp8_swiglu_quant(const void* gate, const void* up, int64_t ld, int
     return end_launch();
 }
 
+fp8lin_status fp8_mlp_fwd(const void* x, const void* gamma, float eps, const uint8_t* wgu, const float* sgu,
+                          const uint8_t* wdown, const float* sdown, int64_t T, int64_t K, int64_t F, uint8_t* xq,
+                          float* sx, float* rstd, void* gu, uint8_t* hq, float* sh, void* y, void* stream)
+{
+    if (T < 0 || K < 0 || F < 0 || K % kGroup != 0 || F % kGroup != 0 || K > 16384 || (T + 3) / 4 > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 3.4028234663852886e38f)
+        return FP8LIN_ERR_ARG;
+    int64_t F2, bx, bg, bxq, bsx, br, bwgu, bsgu, bwd, bsd, bgu, bhq, bsh, by, ng, nb1, nb2;
+    if (!mul_ok(F, 2, &F2) || !bytes_of(T, K, 2, &bx) || !bytes_of(K, 1, 2, &bg) || !bytes_of(T, K, 1, &bxq) ||
+        !bytes_of(T, K / kGroup, 4, &bsx) || !bytes_of(T, 1, 4, &br) || !bytes_of(F2, K, 1, &bwgu) ||
+        !bytes_of(F2 / kGroup, K / kGroup, 4, &bsgu) || !bytes_of(K, F, 1, &bwd) ||
+        !bytes_of(K / kGroup, F / kGroup, 4, &bsd) || !bytes_of(T, F2, 2, &bgu) || !bytes_of(T, F, 1, &bhq) ||
+        !bytes_of(T, F / kGroup, 4, &bsh) || !bytes_of(T, K, 2, &by) || !mul_ok(T, F / kGroup, &ng) ||
+        ng >= ((int64_t)1 << 32) || !mul_ok((T + 127) / 128, (F2 + 127) / 128, &nb1) || nb1 > kMaxBlocks ||
+        !mul_ok((T + 127) / 128, (K + 127) / 128, &nb2) || nb2 > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    if (T == 0 || K == 0 || F == 0) {
+        // nothing to compute except y = 0 when the intermediate width is 0
+        if (T == 0 || K == 0)
+            return FP8LIN_OK;
+        const Buf in0[] = {{x, bx}};
+        const Buf out0[] = {{y, by}};
+        fp8lin_status s0 = check_buffers(in0, 1, out0, 1);
+        if (s0 != FP8LIN_OK)
+            return s0;
+        if ((s0 = begin_launch()) != FP8LIN_OK)
+            return s0;
+        fp8lin::launch_fill_zero_bf16(y, T * K, as_stream(stream));
+        return end_launch();
+    }
+    const Buf in[] = {{x, bx}, {gamma, bg}, {wgu, bwgu}, {sgu, bsgu}, {wdown, bwd}, {sdown, bsd}};
+    const Buf out[] = {{xq, bxq}, {sx, bsx}, {rstd, rstd ? br : 0}, {gu, bgu}, {hq, bhq}, {sh, bsh}, {y, by}};
+    fp8lin_status s = check_buffers(in, 6, out, 7);
+    if (s != FP8LIN_OK)
+        return s;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    const hipStream_t st = as_stream(stream);
+    const uint16_t* gup = static_cast<const uint16_t*>(gu);
+    fp8lin::launch_rmsnorm_quant(x, gamma, T, K, eps, xq, sx, rstd, st);
+    fp8lin::launch_gemm_fwd(xq, sx, wgu, sgu, T, F2, K, gu, st);
+    fp8lin::launch_swiglu_quant(gup, gup + F, F2, T, F, hq, sh, st);
+    fp8lin::launch_gemm_fwd(hq, sh, wdown, sdown, T, K, F, y, st);
+    return end_launch();
+}
+
 fp8lin_status fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t T,
                              int64_t N, int64_t K, void* dx, void* stream)
 {

@@ -271,6 +271,34 @@ fp8lin_status fp8_swiglu_quant(const void* gate, const void* up, int64_t ld, int
                                uint8_t* hq, float* sh, void* stream);
 
 /*
+ * Forward pass of an FP8 MLP block (RMSNorm, gate/up projection, SwiGLU,
+ * down projection) in one call: the unified FP8 flow of the Jet-RL summary
+ * ("Core architecture": rollout and training forward share it; "Quantization
+ * scheme": FP8 GEMMs with 1x128 activation and 128x128 weight quantization,
+ * FP8 activations saved for the backward pass, produced fused with the
+ * operator before each linear layer).  Enqueues, in order:
+ *   fp8_rmsnorm_quant(x, gamma, eps)           -> xq, sx, rstd
+ *   fp8_gemm_fwd(xq, sx, wgu, sgu)             -> gu  = [gate | up], BF16 [T, 2F]
+ *   fp8_swiglu_quant(gu[:, :F], gu[:, F:])     -> hq, sh
+ *   fp8_gemm_fwd(hq, sh, wdown, sdown)         -> y, BF16 [T, K]
+ * and its outputs are bit-identical to those four calls.
+ *   x      : BF16 [T,K] (input);  gamma : BF16 [K];  eps : finite, >= 0
+ *   wgu    : uint8 [2F,K], sgu : float [2F/128][K/128]  (rows 0..F-1 gate, F..2F-1 up)
+ *   wdown  : uint8 [K,F],  sdown : float [K/128][F/128]
+ *   xq, sx, rstd (may be NULL) : as fp8_rmsnorm_quant (saved for the backward pass)
+ *   gu     : BF16 [T,2F] (output; kept for SwiGLU's backward)
+ *   hq, sh : uint8 [T,F], float [T][F/128] (output; saved FP8 input of the down projection)
+ *   y      : BF16 [T,K] (output)
+ * K % 128 == 0, K <= 16384, F % 128 == 0, else FP8LIN_ERR_SHAPE; eps as
+ * fp8_rmsnorm_quant.  T == 0 or K == 0 is an OK no-op; F == 0 writes y = 0.
+ */
+fp8lin_status fp8_mlp_fwd(const void* x, const void* gamma, float eps,
+                          const uint8_t* wgu, const float* sgu, const uint8_t* wdown, const float* sdown,
+                          int64_t T, int64_t K, int64_t F,
+                          uint8_t* xq, float* sx, float* rstd, void* gu, uint8_t* hq, float* sh,
+                          void* y, void* stream);
+
+/*
  * DGrad GEMM (NN):  dX = dY W, contracted over W's row dimension N.
  * Jet-RL summary, "Quantization scheme": the backward DGrad GEMM runs in FP8.
  *   dX[t,k] = sum_g sdy[t][g] * sw[g][k/128] * sum_{n in g} dec(dyq[t,n]) dec(wq[n,k])

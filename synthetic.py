@@ -97,7 +97,8 @@ def random_scales(shape, seed: int, tid: int, lo: float = 1e-3, hi: float = 2e-2
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str          # "forward", "backward" or "producers"
+    kind: str          # "forward", "backward", "producers" or "mlp"
+    # mlp: M tokens, N intermediate width F, K hidden width
     M: int             # tokens (T for backward)
     N: int
     K: int
@@ -116,6 +117,12 @@ WORKLOADS = {
                          "8B-shaped MLP backward, dY[8192,14336] X[8192,4096] W[14336,4096]"),
     "large": Workload("large", "forward", 16384, 27648, 5120, n_outliers(5120),
                       "32B-shaped MLP forward, X[16384,5120] W[27648,5120]"),
+    "mlp": Workload("mlp", "mlp", 8192, 14336, 4096, n_outliers(4096),
+                    "8B-shaped FP8 MLP block forward on 8192 tokens: RMSNorm->FP8, gate/up GEMM [28672,4096], "
+                    "SwiGLU->FP8, down GEMM [4096,14336]"),
+    "mlp_decode": Workload("mlp_decode", "mlp", 64, 14336, 4096, n_outliers(4096),
+                           "8B-shaped FP8 MLP block rollout decode step on 64 tokens: RMSNorm->FP8, gate/up GEMM "
+                           "[28672,4096], SwiGLU->FP8, down GEMM [4096,14336], weights pre-quantized and packed"),
     "producers": Workload("producers", "producers", 8192, 14336, 4096, n_outliers(4096),
                           "8B-shaped producers fused with 1x128 quantization: RMSNorm of X[8192,4096], "
                           "SwiGLU of the gate/up halves of one [8192,2x14336] projection output"),

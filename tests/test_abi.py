@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
               "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
               "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
-              "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_mlp_fwd", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -209,6 +209,32 @@ def test_swiglu_quant_validation(L):
     assert L.fp8_swiglu_quant(A, A + 256, 512, 4, 256, C, D, s0) == DEVICE    # halves of one tensor
     assert L.fp8_swiglu_quant(None, None, 256, 0, 256, None, None, s0) == OK
     assert L.fp8_swiglu_quant(A, B, 256, 4, 256, C, D, s0) == DEVICE
+
+
+@fake_ptrs
+def test_mlp_fwd_validation(L):
+    P = [0x10000000 * (i + 1) for i in range(14)]
+    x, g, wgu, sgu, wd, sd, xq, sx, r, gu, hq, sh, y = P[:13]
+
+    def call(T, K, F, eps=1e-6, **kw):
+        a = dict(x=x, g=g, wgu=wgu, sgu=sgu, wd=wd, sd=sd, xq=xq, sx=sx, r=r, gu=gu, hq=hq, sh=sh, y=y)
+        a.update(kw)
+        return L.fp8_mlp_fwd(a["x"], a["g"], eps, a["wgu"], a["sgu"], a["wd"], a["sd"], T, K, F, a["xq"],
+                             a["sx"], a["r"], a["gu"], a["hq"], a["sh"], a["y"], s0)
+    assert call(4, 100, 128) == SHAPE
+    assert call(4, 128, 100) == SHAPE
+    assert call(4, 16512, 128) == SHAPE
+    assert call(-1, 128, 128) == SHAPE
+    assert call(4, 128, 128, eps=-1.0) == ARG
+    assert call(4, 128, 128, wd=None) == NULL
+    assert call(4, 128, 128, gu=None) == NULL
+    assert call(4, 128, 128, hq=hq + 4) == ALIGN
+    assert call(4, 128, 128, y=wgu) == ALIAS
+    assert call(4, 128, 128, gu=xq + 128) == ALIAS
+    assert call(0, 128, 128, x=None, g=None, wgu=None, sgu=None, wd=None, sd=None, xq=None, sx=None, r=None,
+                gu=None, hq=None, sh=None, y=None) == OK
+    assert call(4, 128, 128, r=None) == DEVICE
+    assert call(4, 128, 128) == DEVICE
 
 
 @fake_ptrs
