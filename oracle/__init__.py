@@ -66,11 +66,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm.argtypes = [i64, i64, i64, f64p, i64, i64, f64p, i64, i64, f64p]
         L.oracle_rmsnorm_bf16.argtypes = [u16p, u16p, i64, i64, ctypes.c_float, u16p, f32p]
         L.oracle_swiglu_bf16.argtypes = [u16p, u16p, i64, i64, i64, u16p, u8p]
+        L.oracle_swiglu_bwd_bf16.argtypes = [u16p, u16p, u16p, i64, i64, i64, u16p, u8p]
         L.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_quant_act", "oracle_quant_weight", "oracle_quant_transpose_bf16",
                   "oracle_quant_transpose_fp8", "oracle_dequant_rowgroup",
                   "oracle_dequant_block", "oracle_gemm", "oracle_rmsnorm_bf16",
-                  "oracle_swiglu_bf16"):
+                  "oracle_swiglu_bf16", "oracle_swiglu_bwd_bf16"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -194,6 +195,19 @@ def swiglu_bf16(gate_bf16: np.ndarray, up_bf16: np.ndarray):
     lib().oracle_swiglu_bf16(_ptr(g, ctypes.c_uint16), _ptr(u, ctypes.c_uint16), F, M, F,
                              _ptr(h, ctypes.c_uint16), _ptr(t, ctypes.c_uint8))
     return h, t.astype(bool)
+
+
+def swiglu_bwd_bf16(gate_bf16: np.ndarray, up_bf16: np.ndarray, dh_bf16: np.ndarray):
+    """Backward of h = silu(g) * u for bf16 [M,F] g, u and dh, evaluated in fp64:
+    returns (dgu bf16 bits [M,2F] = [d_gate | d_up], near_tie bool [M,2F])."""
+    g, u, d = _bits16(gate_bf16), _bits16(up_bf16), _bits16(dh_bf16)
+    assert g.shape == u.shape == d.shape and g.ndim == 2
+    M, F = g.shape
+    out = np.empty((M, 2 * F), np.uint16)
+    t = np.empty((M, 2 * F), np.uint8)
+    lib().oracle_swiglu_bwd_bf16(_ptr(g, ctypes.c_uint16), _ptr(u, ctypes.c_uint16), _ptr(d, ctypes.c_uint16),
+                                 F, M, F, _ptr(out, ctypes.c_uint16), _ptr(t, ctypes.c_uint8))
+    return out, t.astype(bool)
 
 
 def rmsnorm_quant(x_bf16: np.ndarray, gamma_bf16: np.ndarray, eps: float):

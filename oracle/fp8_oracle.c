@@ -361,6 +361,23 @@ void oracle_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t M, in
     }
 }
 
+/* Flag for a fp64 value whose BF16 rounding is within 2^-44 (relative) of a
+ * midpoint between two BF16 neighbours (either neighbour is then correct). */
+static uint8_t bf16_near_tie(double v)
+{
+    double a = fabs(v);
+    if (a == 0.0 || !isfinite(a))
+        return 0;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;
+    if (E < -126)
+        E = -126;
+    double t = a / ldexp(1.0, E - 7);                     /* exact: a in BF16 quanta */
+    double d = fabs((t - floor(t)) - 0.5);
+    return d <= ldexp(t, -44);
+}
+
 /*
  * SwiGLU of BF16 gate / up rows, BF16 output: h = bf16_rne(v) with
  * v = (g / (1 + exp(-g))) * u evaluated in fp64 (C library exp, IEEE
@@ -380,20 +397,41 @@ void oracle_swiglu_bf16(const uint16_t* g, const uint16_t* u, int64_t ld, int64_
             double uv = (double)oracle_bf16_to_f32(u[m * ld + f]);
             double v = (gv / (1.0 + exp(-gv))) * uv;
             h[m * F + f] = oracle_f64_to_bf16(v);
-            uint8_t flag = 0;
-            double a = fabs(v);
-            if (a != 0.0 && isfinite(a)) {
-                int e2;
-                frexp(a, &e2);
-                int E = e2 - 1;
-                if (E < -126)
-                    E = -126;
-                double t = a / ldexp(1.0, E - 7);                 /* exact: a in BF16 quanta */
-                double d = fabs((t - floor(t)) - 0.5);
-                flag = d <= ldexp(t, -44);
-            }
             if (near_tie)
-                near_tie[m * F + f] = flag;
+                near_tie[m * F + f] = bf16_near_tie(v);
+        }
+}
+
+/*
+ * Backward of SwiGLU h = silu(g) * u for BF16 gate g, up u and output
+ * gradient dh (gradients between operators stay BF16).  With
+ * s = 1 / (1 + exp(-g)) and silu(g) = g * s, the textbook derivatives
+ *   d_up   = dh * silu(g)
+ *   d_gate = dh * u * s * (1 + g * (1 - s))
+ * are evaluated in fp64 (C library exp, IEEE operations in that order) and
+ * rounded once to BF16.  Output dgu is [M, 2F]: d_gate in columns [0, F),
+ * d_up in [F, 2F) (the layout of the fused gate/up projection).  near_tie
+ * ([M, 2F], may be NULL) flags values within 2^-44 of a BF16 midpoint.
+ * g, u and dh have row stride ld (elements).
+ */
+void oracle_swiglu_bwd_bf16(const uint16_t* g, const uint16_t* u, const uint16_t* dh, int64_t ld, int64_t M,
+                            int64_t F, uint16_t* dgu, uint8_t* near_tie)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t f = 0; f < F; ++f) {
+            double gv = (double)oracle_bf16_to_f32(g[m * ld + f]);
+            double uv = (double)oracle_bf16_to_f32(u[m * ld + f]);
+            double dv = (double)oracle_bf16_to_f32(dh[m * ld + f]);
+            double s = 1.0 / (1.0 + exp(-gv));
+            double d_up = dv * (gv * s);
+            double d_gate = ((dv * uv) * s) * (1.0 + gv * (1.0 - s));
+            dgu[m * 2 * F + f] = oracle_f64_to_bf16(d_gate);
+            dgu[m * 2 * F + F + f] = oracle_f64_to_bf16(d_up);
+            if (near_tie) {
+                near_tie[m * 2 * F + f] = bf16_near_tie(d_gate);
+                near_tie[m * 2 * F + F + f] = bf16_near_tie(d_up);
+            }
         }
 }
 

@@ -258,3 +258,74 @@ def test_swiglu_quant_is_quant_of_output():
     h, near2 = oracle.swiglu_bf16(gb, ub)
     q2, s2 = oracle.quant_act(h)
     assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(near, near2)
+
+
+# --------------------------------------------------------- SwiGLU backward
+
+def exact_swiglu_bwd(gv: float, uv: float, dv: float):
+    """(d_gate, d_up) of h = silu(g) u from 60-digit decimal arithmetic, each
+    as (bf16 value, relative distance to the nearest bf16 midpoint)."""
+    getcontext().prec = 60
+    g, u, d = Decimal(gv), Decimal(uv), Decimal(dv)
+    s = 1 / (1 + (-g).exp())
+    d_up = Fraction(d * g * s)
+    d_gate = Fraction(d * u * s * (1 + g * (1 - s)))
+    return [(round_fraction(q, 8, -126), midpoint_distance(q, 8, -126)) for q in (d_gate, d_up)]
+
+
+def test_swiglu_bwd_matches_high_precision():
+    """Both gradients equal bf16 of the exact derivative from 60-digit decimal
+    arithmetic wherever that value is not within 2^-40 of a midpoint (pins
+    sigmoid, its derivative 1 + g (1 - s), which factor each output takes,
+    and the [d_gate | d_up] layout)."""
+    gb, ub = swiglu_cases()
+    rng = np.random.default_rng(21)
+    db = bf16(rng.normal(0, 1e-3, gb.shape).astype(np.float32) * np.where(rng.random(gb.shape) < 0.1, 1e3, 1.0))
+    out, near = oracle.swiglu_bwd_bf16(gb, ub, db)
+    R, F = gb.shape
+    gf, uf, dfl = f32(gb), f32(ub), f32(db)
+    of = f32(out)
+    checked = 0
+    for r in range(R):
+        for c in range(F):
+            for j, (want, dist) in enumerate(exact_swiglu_bwd(float(gf[r, c]), float(uf[r, c]), float(dfl[r, c]))):
+                col = c + j * F
+                if dist <= Fraction(1, 2 ** 40):
+                    continue
+                assert not near[r, col]
+                assert Fraction(float(of[r, col])) == want, (r, c, j, gf[r, c], uf[r, c], dfl[r, c], of[r, col])
+                checked += 1
+    assert checked > 0.99 * 2 * gf.size
+
+
+def test_swiglu_bwd_library_autograd():
+    """Against torch autograd of silu(g) * u in float64, rounded to fp32 then
+    bf16 by library casts (elements whose fp32 value is exactly a bf16 midpoint
+    are skipped: there the double rounding may differ)."""
+    M, F = 32, 1024
+    gb = synthetic.activations(M, F, seed=14, n_out=2)
+    ub = synthetic.activations(M, F, seed=15, n_out=0)
+    db = synthetic.grad_out(M, F, seed=16)
+    out, near = oracle.swiglu_bwd_bf16(gb, ub, db)
+    g = torch.from_numpy(f32(gb).astype(np.float64)).requires_grad_(True)
+    u = torch.from_numpy(f32(ub).astype(np.float64)).requires_grad_(True)
+    h = torch.nn.functional.silu(g) * u
+    h.backward(torch.from_numpy(f32(db).astype(np.float64)))
+    want = np.concatenate([g.grad.numpy(), u.grad.numpy()], axis=1).astype(np.float32)
+    ok = ((want.view(np.uint32) & 0xFFFF) != 0x8000) & ~near
+    assert np.array_equal(out[ok], torch_bf16_bits(want)[ok])
+    assert ok.mean() > 0.999
+
+
+def test_swiglu_bwd_special_values():
+    """g = 0: d_up = 0 and d_gate = dh u / 2 exactly; large positive g:
+    d_up = dh g and d_gate = dh u; large negative g: both vanish."""
+    F = 128
+    gb = bf16(np.array([[0.0] * 32 + [128.0] * 32 + [-1000.0] * 32 + [0.0] * 32]))
+    ub = bf16(np.full((1, F), 3.0))
+    db = bf16(np.full((1, F), -0.5))
+    out, _ = oracle.swiglu_bwd_bf16(gb, ub, db)
+    dg, du = f32(out[0, :F]), f32(out[0, F:])
+    assert np.all(dg[:32] == -0.75) and np.all(du[:32] == 0.0)
+    assert np.all(dg[32:64] == -1.5) and np.all(du[32:64] == -64.0)
+    assert np.all(dg[64:96] == 0.0) and np.all(du[64:96] == 0.0)
