@@ -172,6 +172,55 @@ def build_step(name, torch, fl, synthetic):
         st.config = {"workload": wl.doc, "T": T, "K": K, "F": F, "eps": 1e-6, "outlier_columns": wl.n_out,
                      "weight_copies_rotated": st.rotate,
                      "same_kernels_as": "fp8_mlp_fwd (one call; bit-identical outputs)"}
+    elif wl.kind == "mlp_train":
+        T, F, K = wl.M, wl.N, wl.K
+        x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
+        gamma = bf16(synthetic.norm_weights(K, seed=0))
+        dy = bf16(synthetic.grad_out(T, K, seed=0))
+        wgu, sgu = fl.fp8_quant_weight(bf16(synthetic.weights(2 * F, K, seed=0)))
+        wd, sd = fl.fp8_quant_weight(bf16(synthetic.weights(K, F, seed=1)))
+        wguT, sguT = fl.fp8_weight_transpose(wgu, sgu)     # made with the weight quantization
+        wdT, sdT = fl.fp8_weight_transpose(wd, sd)
+        torch.cuda.synchronize()
+        xq, sx, rstd = empty((T, K), u8), empty((T, K // G), f32), empty((T,), f32)
+        gu, hq, sh, y = empty((T, 2 * F), bf), empty((T, F), u8), empty((T, F // G), f32), empty((T, K), bf)
+        dyTq, sdyT, dyq, sdy = empty((K, T), u8), empty((K, T // G), f32), empty((T, K), u8), empty((T, K // G), f32)
+        hTq, shT = empty((F, T), u8), empty((F, T // G), f32)
+        dwd, dh, dgu = empty((K, F), bf), empty((T, F), bf), empty((T, 2 * F), bf)
+        dguTq, sdguT = empty((2 * F, T), u8), empty((2 * F, T // G), f32)
+        dguq, sdgu = empty((T, 2 * F), u8), empty((T, 2 * F // G), f32)
+        xTq, sxT = empty((K, T), u8), empty((K, T // G), f32)
+        dwgu, dxn = empty((2 * F, K), bf), empty((T, K), bf)
+        dual = lambda r, c: r * c * 2 + 2 * r * c + (c * (r // G) + r * (c // G)) * 4
+        requant = lambda r, c: 2 * r * c + (r * (c // G) + c * (r // G)) * 4
+        st.add("rmsnorm_quant", lambda i: fl.fp8_rmsnorm_quant(x, gamma, 1e-6, out=(xq, sx, rstd)), "hbm",
+               act_quant_bytes(T, K) + 4 * T + 2 * K)
+        st.add("gemm_gate_up", lambda i: fl.fp8_gemm_fwd(xq, sx, wgu, sgu, out=gu), "mfma", 4 * T * F * K)
+        st.add("swiglu_quant", lambda i: fl.fp8_swiglu_quant(gu[:, :F], gu[:, F:], out=(hq, sh)), "hbm",
+               2 * T * F * 2 + T * F + T * (F // G) * 4)
+        st.add("gemm_down", lambda i: fl.fp8_gemm_fwd(hq, sh, wd, sd, out=y), "mfma", 2 * T * K * F)
+        st.add("quant_transpose_dual_dY", lambda i: fl.fp8_quant_transpose(dy, dual=True, out=(dyTq, sdyT, dyq, sdy)),
+               "hbm", dual(T, K))
+        st.add("quant_transpose_fp8_H", lambda i: fl.fp8_quant_transpose(hq, sh, out=(hTq, shT, None, None)), "hbm",
+               requant(T, F))
+        st.add("gemm_wgrad_down", lambda i: fl.fp8_gemm_wgrad(dyTq, sdyT, hTq, shT, out=dwd), "mfma", 2 * T * K * F)
+        st.add("gemm_dgrad_down", lambda i: fl.fp8_gemm_dgrad_t(dyq, sdy, wdT, sdT, out=dh), "mfma", 2 * T * K * F)
+        st.add("swiglu_bwd", lambda i: fl.fp8_swiglu_bwd(gu[:, :F], gu[:, F:], dh, out=dgu), "hbm",
+               3 * T * F * 2 + 2 * T * F * 2)
+        st.add("quant_transpose_dual_dGU",
+               lambda i: fl.fp8_quant_transpose(dgu, dual=True, out=(dguTq, sdguT, dguq, sdgu)), "hbm", dual(T, 2 * F))
+        st.add("quant_transpose_fp8_X", lambda i: fl.fp8_quant_transpose(xq, sx, out=(xTq, sxT, None, None)), "hbm",
+               requant(T, K))
+        st.add("gemm_wgrad_gate_up", lambda i: fl.fp8_gemm_wgrad(dguTq, sdguT, xTq, sxT, out=dwgu), "mfma",
+               4 * T * F * K)
+        st.add("gemm_dgrad_gate_up", lambda i: fl.fp8_gemm_dgrad_t(dguq, sdgu, wguT, sguT, out=dxn), "mfma",
+               4 * T * F * K)
+        st.dominant = None
+        st.gemm_flop = 18 * T * K * F
+        st.config = {"workload": wl.doc, "T": T, "K": K, "F": F, "eps": 1e-6, "outlier_columns": wl.n_out,
+                     "same_kernels_as": "fp8_mlp_fwd + fp8_mlp_bwd",
+                     "dgrad_weights": "transposed FP8 copies (fp8_weight_transpose), made with the weight "
+                                      "quantization outside the step"}
     elif wl.kind == "producers":
         T, F, K = wl.M, wl.N, wl.K
         x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
@@ -274,7 +323,7 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
             oracle.gemm_fwd(xq, sx, wq, sw)
         what = ("%d of %d rows of X per repetition: oracle 1x128 quantization + fp64 GEMM against "
                 "the full W (W quantized once, outside the timing)" % (rows, M))
-    elif wl.kind == "mlp":
+    elif wl.kind in ("mlp", "mlp_train"):
         T, F, K = wl.M, wl.N, wl.K
         rows = min(T, 8)
         x = synthetic.activations(T, K, seed=0, n_out=wl.n_out)[:rows]
@@ -298,7 +347,9 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
         return {"value": flop * reps / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
                 "sample": "%d of %d token rows per repetition through the oracle block: RMSNorm + quantization, "
                           "fp64 gate/up GEMM, bf16 rounding, SwiGLU + quantization, fp64 down GEMM (weights "
-                          "quantized once, outside the timing); %d repetitions" % (rows, T, reps),
+                          "quantized once, outside the timing); %d repetitions%s" % (
+                              rows, T, reps, "; forward only: its oracle GEMM rate stands for the training step's"
+                              if wl.kind == "mlp_train" else ""),
                 "seconds": round(dt, 2)}
     elif wl.kind == "producers":
         T, F, K = wl.M, wl.N, wl.K
@@ -369,6 +420,13 @@ KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes f
     "gemm_dgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_wgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_wgrad_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_dgrad_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_wgrad_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_dgrad_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "quant_transpose_fp8_H": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "quant_transpose_dual_dGU": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "swiglu_bwd": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "gemm_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "rmsnorm_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
@@ -384,6 +442,13 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "gemm_fwd": "gemm_",
     "gemm_dgrad": "Mode)0",     # the backward step runs DGrad as the NT GEMM on W^T
     "gemm_wgrad": "Mode)2",
+    "gemm_wgrad_down": None,    # GEMMs of one kernel at several shapes: counters cannot tell them apart
+    "gemm_dgrad_down": None,
+    "gemm_wgrad_gate_up": None,
+    "gemm_dgrad_gate_up": None,
+    "quant_transpose_fp8_H": None,
+    "quant_transpose_dual_dGU": None,
+    "swiglu_bwd": "swiglu_bwd_kernel",
     "gemm_gate_up": None,       # same kernel as gemm_down: counters cannot tell them apart
     "gemm_down": None,
     "rmsnorm_quant": "rmsnorm_quant_kernel",
@@ -467,7 +532,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny", "producers", "mlp", "mlp_decode"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny", "producers", "mlp", "mlp_decode",
+                             "mlp_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-eager", action="store_true",
                     help="run each kernel of the step eagerly (for rocprofv3 counter passes) and exit")

@@ -22,7 +22,7 @@ __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
     "fp8_gemm_fwd", "fp8_gemm_fwd_packed", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
-    "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_mlp_fwd",
+    "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -60,6 +60,8 @@ _SYMBOLS = {
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "fp8_swiglu_quant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "fp8_swiglu_bwd": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "fp8_mlp_fwd": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float] + [ctypes.c_void_p] * 4 +
                     [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 8, ctypes.c_int),
     "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
@@ -318,6 +320,31 @@ def fp8_swiglu_quant(gate, up, out=None, stream=None):
     return q, s
 
 
+def fp8_swiglu_bwd(gate, up, dh, out=None, stream=None):
+    """BF16 gradients of silu(gate) * up given dh bf16 [M,F]: returns dgu bf16
+    [M,2F] = [d_gate | d_up].  gate and up may be row-strided views (e.g. the
+    two halves of the saved [M,2F] gate/up output) with equal row strides."""
+    if gate.shape != up.shape or gate.dim() != 2:
+        raise ValueError("gate and up must be 2-D tensors of one shape")
+    M, F = gate.shape
+    _expect(dh, "dh", torch.bfloat16, (M, F))
+    for t, name in ((gate, "gate"), (up, "up")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be torch.bfloat16" % name)
+        if t.numel() and not t.is_cuda:
+            raise ValueError("%s must be on the GPU" % name)
+        if M and F and t.stride(1) != 1:
+            raise ValueError("%s must have unit column stride" % name)
+    ld = gate.stride(0) if M > 1 else F
+    if M > 1 and up.stride(0) != ld:
+        raise ValueError("gate and up must have the same row stride")
+    dgu = out if out is not None else _empty((M, 2 * F), torch.bfloat16, dh)
+    _expect(dgu, "dgu", torch.bfloat16, (M, 2 * F))
+    _check(lib().fp8_swiglu_bwd(_ptr(gate), _ptr(up), ld, _ptr(dh), M, F, _ptr(dgu), _stream(stream)),
+           "fp8_swiglu_bwd")
+    return dgu
+
+
 def fp8_mlp_fwd(x, gamma, wgu, sgu, wdown, sdown, eps: float = 1e-6, out=None, rstd: bool = True, stream=None):
     """Forward pass of an FP8 MLP block: RMSNorm -> gate/up GEMM -> SwiGLU -> down GEMM.
 
@@ -353,6 +380,41 @@ def fp8_mlp_fwd(x, gamma, wgu, sgu, wdown, sdown, eps: float = 1e-6, out=None, r
                              T, K, F, _ptr(out["xq"]), _ptr(out["sx"]), _ptr(out["rstd"]), _ptr(out["gu"]),
                              _ptr(out["hq"]), _ptr(out["sh"]), _ptr(out["y"]), _stream(stream)), "fp8_mlp_fwd")
     return out
+
+
+def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, stream=None):
+    """Backward pass of the FP8 MLP block through its three linear layers, as a
+    fixed sequence of C-ABI calls on one stream (every step runs in the
+    library's kernels; this function only allocates the intermediates):
+
+      fp8_quant_transpose(dy, dual)           -> dYq (1x128), dY^T q (128 along T)
+      fp8_quant_transpose(hq, sh)             -> H^T q        (saved FP8 SwiGLU output)
+      fp8_gemm_wgrad(dY^T q, H^T q)           -> dw_down [K,F]
+      fp8_gemm_dgrad_t(dYq, W_down^T)         -> dh [T,F]
+      fp8_swiglu_bwd(gate, up, dh)            -> dgu [T,2F]   (BF16)
+      fp8_quant_transpose(dgu, dual)          -> dGUq, dGU^T q
+      fp8_quant_transpose(xq, sx)             -> X^T q        (saved FP8 block input)
+      fp8_gemm_wgrad(dGU^T q, X^T q)          -> dw_gu [2F,K]
+      fp8_gemm_dgrad_t(dGUq, W_gu^T)          -> dxn [T,K]    (gradient of the RMSNorm output)
+
+    dy bf16 [T,K]; saved is the dict returned by fp8_mlp_fwd; wguT/sguT and
+    wdT/sdT are the transposed weight copies (fp8_weight_transpose of the
+    fused gate/up and down weights).  T % 128 == 0 (WGrad groups run along T).
+    Returns dict(dxn, dw_gu, dw_down, dh, dgu)."""
+    T, K = dy.shape
+    F = saved["hq"].shape[1]
+    st = stream
+    dyTq, sdyT, dyq, sdy = fp8_quant_transpose(dy, dual=True, stream=st)
+    hTq, shT = fp8_quant_transpose(saved["hq"], saved["sh"], stream=st)
+    dw_down = fp8_gemm_wgrad(dyTq, sdyT, hTq, shT, stream=st)
+    dh = fp8_gemm_dgrad_t(dyq, sdy, wdT, sdT, stream=st)
+    gu = saved["gu"]
+    dgu = fp8_swiglu_bwd(gu[:, :F], gu[:, F:], dh, stream=st)
+    dguTq, sguT_, dguq, sdgu = fp8_quant_transpose(dgu, dual=True, stream=st)
+    xTq, sxT = fp8_quant_transpose(saved["xq"], saved["sx"], stream=st)
+    dw_gu = fp8_gemm_wgrad(dguTq, sguT_, xTq, sxT, stream=st)
+    dxn = fp8_gemm_dgrad_t(dguq, sdgu, wguT, sguT, stream=st)
+    return {"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh, "dgu": dgu}
 
 
 def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):

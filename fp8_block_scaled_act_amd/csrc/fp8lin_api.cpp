@@ -447,6 +447,32 @@ fp8lin_status fp8_swiglu_quant(const void* gate, const void* up, int64_t ld, int
     return end_launch();
 }
 
+fp8lin_status fp8_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void* dh, int64_t M, int64_t F,
+                             void* dgu, void* stream)
+{
+    if (M < 0 || F < 0 || F % kGroup != 0 || ld < F)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bdh, bout, span;
+    if (!bytes_of(M, F, 2, &bdh) || !bytes_of(M, 2 * F, 2, &bout))
+        return FP8LIN_ERR_SHAPE;
+    if (bdh == 0)
+        return FP8LIN_OK;
+    if (!mul_ok(M - 1, ld, &span) || span > INT64_MAX / 2 - F)
+        return FP8LIN_ERR_SHAPE;
+    const int64_t bin = (span + F) * 2;
+    if (ld % 8 != 0)
+        return FP8LIN_ERR_ALIGN;
+    const Buf in[] = {{gate, bin}, {up, bin}, {dh, bdh}};
+    const Buf out[] = {{dgu, bout}};
+    fp8lin_status s = check_buffers(in, 3, out, 1);
+    if (s != FP8LIN_OK)
+        return s;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_swiglu_bwd(gate, up, ld, dh, M, F, dgu, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_mlp_fwd(const void* x, const void* gamma, float eps, const uint8_t* wgu, const float* sgu,
                           const uint8_t* wdown, const float* sdown, int64_t T, int64_t K, int64_t F, uint8_t* xq,
                           float* sx, float* rstd, void* gu, uint8_t* hq, float* sh, void* y, void* stream)

@@ -305,6 +305,49 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
     }
 }
 
+// ======================================================== SwiGLU backward
+//
+// BF16 gradients of h = silu(g) u (gradients between operators stay BF16):
+// s = 1 / (1 + exp(-g)), d_up = dh (g s), d_gate = ((dh u) s) (1 + g (1 - s)),
+// each evaluated in fp64 in that order and rounded once to BF16.  A thread
+// owns 8 consecutive columns of one row (16-byte loads of g, u, dh; 16-byte
+// stores of d_gate into dgu[:, :F] and d_up into dgu[:, F:]).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restrict__ gate,
+                                                         const uint16_t* __restrict__ up, int64_t ld,
+                                                         const uint16_t* __restrict__ dh, int64_t F,
+                                                         int64_t nchunks, uint16_t* __restrict__ dgu)
+{
+    const int64_t cpr = F >> 3;                             // 8-column chunks per row
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += (int64_t)gridDim.x * 256) {
+        const int64_t m = i / cpr, c = (i - m * cpr) * 8;
+        const uint4 gv = load_nt(gate + m * ld + c);
+        const uint4 uv = load_nt(up + m * ld + c);
+        const uint4 dv = load_nt(dh + m * F + c);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+        uint32_t og[4], ou[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t rg[2], ru[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const double g = h ? bf16_hi(gw[j]) : bf16_lo(gw[j]);
+                const double u = h ? bf16_hi(uw[j]) : bf16_lo(uw[j]);
+                const double d = h ? bf16_hi(dw[j]) : bf16_lo(dw[j]);
+                const double sg = 1.0 / (1.0 + exp(-g));
+                rg[h] = f64_to_bf16_rne(((d * u) * sg) * (1.0 + g * (1.0 - sg)));
+                ru[h] = f64_to_bf16_rne(d * (g * sg));
+            }
+            og[j] = rg[0] | (rg[1] << 16);
+            ou[j] = ru[0] | (ru[1] << 16);
+        }
+        uint16_t* row = dgu + m * 2 * F + c;
+        *reinterpret_cast<uint4*>(row) = make_uint4(og[0], og[1], og[2], og[3]);
+        *reinterpret_cast<uint4*>(row + F) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+    }
+}
+
 // ================================================================ launchers
 
 template <int NV>
@@ -347,6 +390,22 @@ void launch_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M
     swiglu_quant_kernel<kUnroll><<<(unsigned)(blocks < 1 ? 1 : blocks), 256, 0, st>>>(
         static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up), ld, GF, ngroups,
         reinterpret_cast<uint2*>(q), s);
+}
+
+}  // namespace fp8lin
+
+namespace fp8lin {
+
+void launch_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void* dh, int64_t M, int64_t F,
+                       void* dgu, hipStream_t st)
+{
+    const int64_t nchunks = M * (F / 8);
+    int64_t blocks = (nchunks + 255) / 256;
+    if (blocks > 32768)
+        blocks = 32768;
+    swiglu_bwd_kernel<<<(unsigned)(blocks < 1 ? 1 : blocks), 256, 0, st>>>(
+        static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up), ld, static_cast<const uint16_t*>(dh),
+        F, nchunks, static_cast<uint16_t*>(dgu));
 }
 
 }  // namespace fp8lin

@@ -271,6 +271,25 @@ fp8lin_status fp8_swiglu_quant(const void* gate, const void* up, int64_t ld, int
                                uint8_t* hq, float* sh, void* stream);
 
 /*
+ * Backward of SwiGLU h = silu(gate) * up, BF16 in and out (Jet-RL summary,
+ * "Quantization scheme": gradients handed between operators stay BF16; the
+ * FP8 quantization of the result for the gate/up DGrad and WGrad GEMMs is
+ * fp8_quant_transpose's dual output).  With s = 1 / (1 + exp(-g)):
+ *   d_up[m,f]   = bf16(dh * (g * s))
+ *   d_gate[m,f] = bf16(((dh * up) * s) * (1 + g * (1 - s)))
+ * evaluated in fp64 in that order and rounded once to nearest even.
+ *   gate, up : BF16, rows of F elements at row stride ld (e.g. the halves of
+ *              the block's saved gate/up output [M, 2F])
+ *   dh       : BF16 [M,F] (input, dense)
+ *   dgu      : BF16 [M,2F] (output): d_gate in columns [0,F), d_up in [F,2F),
+ *              the layout of the fused gate/up projection's output gradient
+ * F % 128 == 0 and ld >= F, else FP8LIN_ERR_SHAPE; ld % 8 != 0:
+ * FP8LIN_ERR_ALIGN.  M == 0 or F == 0 is an OK no-op.
+ */
+fp8lin_status fp8_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void* dh,
+                             int64_t M, int64_t F, void* dgu, void* stream);
+
+/*
  * Forward pass of an FP8 MLP block (RMSNorm, gate/up projection, SwiGLU,
  * down projection) in one call: the unified FP8 flow of the Jet-RL summary
  * ("Core architecture": rollout and training forward share it; "Quantization

@@ -97,7 +97,7 @@ def random_scales(shape, seed: int, tid: int, lo: float = 1e-3, hi: float = 2e-2
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str          # "forward", "backward", "producers" or "mlp"
+    kind: str          # "forward", "backward", "producers", "mlp" or "mlp_train"
     # mlp: M tokens, N intermediate width F, K hidden width
     M: int             # tokens (T for backward)
     N: int
@@ -123,6 +123,11 @@ WORKLOADS = {
     "mlp_decode": Workload("mlp_decode", "mlp", 64, 14336, 4096, n_outliers(4096),
                            "8B-shaped FP8 MLP block rollout decode step on 64 tokens: RMSNorm->FP8, gate/up GEMM "
                            "[28672,4096], SwiGLU->FP8, down GEMM [4096,14336], weights pre-quantized and packed"),
+    "mlp_train": Workload("mlp_train", "mlp_train", 8192, 14336, 4096, n_outliers(4096),
+                          "8B-shaped FP8 MLP block training step on 8192 tokens: forward (RMSNorm->FP8, gate/up "
+                          "GEMM, SwiGLU->FP8, down GEMM) and backward through the three linear layers (dual "
+                          "transpose-quant of dY and dGU, FP8-source requant of H and X, SwiGLU backward, two "
+                          "DGrad and two WGrad GEMMs)"),
     "producers": Workload("producers", "producers", 8192, 14336, 4096, n_outliers(4096),
                           "8B-shaped producers fused with 1x128 quantization: RMSNorm of X[8192,4096], "
                           "SwiGLU of the gate/up halves of one [8192,2x14336] projection output"),

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
               "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
               "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
-              "fp8_mlp_fwd", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -209,6 +209,18 @@ def test_swiglu_quant_validation(L):
     assert L.fp8_swiglu_quant(A, A + 256, 512, 4, 256, C, D, s0) == DEVICE    # halves of one tensor
     assert L.fp8_swiglu_quant(None, None, 256, 0, 256, None, None, s0) == OK
     assert L.fp8_swiglu_quant(A, B, 256, 4, 256, C, D, s0) == DEVICE
+
+
+@fake_ptrs
+def test_swiglu_bwd_validation(L):
+    # gate, up, ld, dh, M, F, dgu
+    assert L.fp8_swiglu_bwd(A, B, 256, C, 4, 100, D, s0) == SHAPE          # F % 128
+    assert L.fp8_swiglu_bwd(A, B, 128, C, 4, 256, D, s0) == SHAPE          # ld < F
+    assert L.fp8_swiglu_bwd(A, B, 260, C, 4, 256, D, s0) == ALIGN
+    assert L.fp8_swiglu_bwd(A, B, 256, None, 4, 256, D, s0) == NULL
+    assert L.fp8_swiglu_bwd(A, B, 256, C, 4, 256, C + 64, s0) == ALIAS     # dgu over dh
+    assert L.fp8_swiglu_bwd(A, A + 256, 512, C, 4, 256, D, s0) == DEVICE   # halves of one tensor
+    assert L.fp8_swiglu_bwd(None, None, 256, None, 0, 256, None, s0) == OK
 
 
 @fake_ptrs

@@ -1,0 +1,172 @@
+"""GPU tests of the SwiGLU backward (fp8_swiglu_bwd) and of the MLP block's
+backward chain (fp8_mlp_bwd).
+
+fp8_swiglu_bwd must be bit-identical to the oracle wherever the exact
+derivative is not next to a BF16 midpoint (the oracle flags such elements;
+groups of 128 holding one are reported and skipped).  The chain is compared
+with the oracle chain computed from the same inputs on the CPU: stage inputs
+differ by the bf16 roundings of GEMM outputs (fp32 vs fp64 accumulation), so
+its tolerance is on the rms-relative error, 1e-2; the per-call parity of
+every call in the chain is covered by the other GPU tests."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_act_amd as fl
+import oracle
+import synthetic
+from gpu_util import DEV, bf16_bits_to_f64, bf16_to_dev, f32_to_dev, first_mismatch, host, say, u8_to_dev
+
+pytestmark = pytest.mark.gpu
+G = 128
+TOL = 1e-2
+
+
+def compare_swiglu_bwd(out, gate, up, dh, what):
+    ref, near = oracle.swiglu_bwd_bf16(gate, up, dh)
+    got = host(out)
+    M, F2 = ref.shape
+    keep = ~near
+    if near.any():
+        print("[%s] %d near-tie element(s) skipped" % (what, near.sum()))
+    bad = first_mismatch(got[keep], ref[keep])
+    assert bad is None, "%s: first mismatch at flat %s gpu=%#x ref=%#x (%d total)" % (what, bad[0], bad[1], bad[2],
+                                                                                     bad[3])
+
+
+@pytest.mark.parametrize("M,F", [(1, 128), (37, 1024), (64, 14336), (300, 640)])
+def test_swiglu_bwd_shapes(M, F):
+    gate = synthetic.activations(M, F, seed=F + 3, n_out=max(1, F // 1024))
+    up = synthetic.activations(M, F, seed=F + 4, n_out=0)
+    dh = synthetic.grad_out(M, F, seed=F + 5)
+    say("swiglu_bwd", M, F)
+    out = fl.fp8_swiglu_bwd(bf16_to_dev(gate), bf16_to_dev(up), bf16_to_dev(dh))
+    compare_swiglu_bwd(out, gate, up, dh, "%dx%d" % (M, F))
+
+
+def test_swiglu_bwd_halves_and_special_values():
+    M, F = 40, 512
+    rng = np.random.default_rng(3)
+    gu = synthetic.activations(M, 2 * F, seed=8, n_out=3)
+    g32 = synthetic.bf16_bits_to_f32(gu)
+    g32[0, :F] = 0.0
+    g32[1, :F] = rng.uniform(60, 800, F) * np.where(rng.random(F) < 0.5, -1, 1)
+    g32[2, :F] = -1.2784645                        # near the zero of silu'
+    gu = synthetic.f32_to_bf16_bits(g32)
+    dh = synthetic.grad_out(M, F, seed=9)
+    say("swiglu_bwd halves")
+    t = bf16_to_dev(gu)
+    out = fl.fp8_swiglu_bwd(t[:, :F], t[:, F:], bf16_to_dev(dh))
+    compare_swiglu_bwd(out, np.ascontiguousarray(gu[:, :F]), np.ascontiguousarray(gu[:, F:]), dh, "halves")
+
+
+def test_swiglu_bwd_full_size():
+    M, F = 8192, 14336
+    gu = synthetic.activations(M, 2 * F, seed=1, n_out=synthetic.n_outliers(2 * F))
+    dh = synthetic.grad_out(M, F, seed=2)
+    say("swiglu_bwd full", M, F)
+    t = bf16_to_dev(gu)
+    out = fl.fp8_swiglu_bwd(t[:, :F], t[:, F:], bf16_to_dev(dh))
+    compare_swiglu_bwd(out, np.ascontiguousarray(gu[:, :F]), np.ascontiguousarray(gu[:, F:]), dh, "8B")
+
+
+def test_swiglu_bwd_degenerate():
+    say("swiglu_bwd empty")
+    z = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    assert fl.fp8_swiglu_bwd(z, z, z).shape == (0, 512)
+
+
+# --------------------------------------------------------- backward chain
+
+def rms_rel(got, ref):
+    ref = np.asarray(ref, np.float64)
+    return float(np.sqrt(np.mean((np.asarray(got, np.float64) - ref) ** 2)) / np.sqrt(np.mean(ref * ref)))
+
+
+def oracle_block_fwd_bwd(x, gamma, wgu, wdown, dy, eps):
+    """The whole block, forward and backward, through the oracle."""
+    owgu, osgu = oracle.quant_weight(wgu)
+    owd, osd = oracle.quant_weight(wdown)
+    xq, sx, _ = oracle.rmsnorm_quant(x, gamma, eps)
+    gu = oracle.f64_to_bf16(oracle.gemm_fwd(xq, sx, owgu, osgu))
+    F = gu.shape[1] // 2
+    g, u = np.ascontiguousarray(gu[:, :F]), np.ascontiguousarray(gu[:, F:])
+    hq, sh, _ = oracle.swiglu_quant(g, u)
+    dyq, sdy = oracle.quant_act(dy)
+    dyTq, sdyT = oracle.quant_transpose_bf16(dy)
+    hTq, shT = oracle.quant_transpose_fp8(hq, sh)
+    dw_down = oracle.gemm_wgrad(dyTq, sdyT, hTq, shT)
+    dh = oracle.f64_to_bf16(oracle.gemm_dgrad(dyq, sdy, owd, osd))
+    dgu, _ = oracle.swiglu_bwd_bf16(g, u, dh)
+    dguq, sdgu = oracle.quant_act(dgu)
+    dguTq, sdguT = oracle.quant_transpose_bf16(dgu)
+    xTq, sxT = oracle.quant_transpose_fp8(xq, sx)
+    dw_gu = oracle.gemm_wgrad(dguTq, sdguT, xTq, sxT)
+    dxn = oracle.gemm_dgrad(dguq, sdgu, owgu, osgu)
+    return {"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh, "dgu": dgu}, (owgu, osgu, owd, osd)
+
+
+@pytest.mark.parametrize("T,K,F", [(256, 256, 384), (384, 512, 256)])
+def test_mlp_backward_chain_small(T, K, F):
+    eps = 1e-6
+    x = synthetic.activations(T, K, seed=T, n_out=2)
+    gamma = synthetic.norm_weights(K, seed=T)
+    wgu = synthetic.weights(2 * F, K, seed=T)
+    wdown = synthetic.weights(K, F, seed=T + 1)
+    dy = synthetic.grad_out(T, K, seed=T)
+    ref, (owgu, osgu, owd, osd) = oracle_block_fwd_bwd(x, gamma, wgu, wdown, dy, eps)
+    say("mlp fwd+bwd chain", T, K, F)
+    wgu_q, sgu = u8_to_dev(owgu), f32_to_dev(osgu)
+    wd_q, sd = u8_to_dev(owd), f32_to_dev(osd)
+    saved = fl.fp8_mlp_fwd(bf16_to_dev(x), bf16_to_dev(gamma), wgu_q, sgu, wd_q, sd, eps=eps)
+    wguT, sguT = fl.fp8_weight_transpose(wgu_q, sgu)
+    wdT, sdT = fl.fp8_weight_transpose(wd_q, sd)
+    grads = fl.fp8_mlp_bwd(bf16_to_dev(dy), saved, wguT, sguT, wdT, sdT)
+    errs = {}
+    for k in ("dh", "dgu", "dxn", "dw_gu", "dw_down"):
+        want = ref[k] if ref[k].dtype == np.float64 else bf16_bits_to_f64(ref[k])
+        errs[k] = rms_rel(bf16_bits_to_f64(host(grads[k])), want)
+    print("[mlp bwd %dx%dx%d] rms-relative errors %s" % (T, K, F, errs))
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_mlp_backward_8B_sampled_rows():
+    """One 8B layer (T 8192, hidden 4096, intermediate 14336): the DGrad path
+    (dh, dgu, dxn) of sampled token rows against the oracle, which needs only
+    those rows of every operand; dw_down and dw_gu checked for finiteness and
+    scale (the WGrad kernels' own full-size parity is tested elsewhere)."""
+    T, K, F = 8192, 4096, 14336
+    eps = 1e-6
+    rows = np.array([0, 5, 1000, 4097, 8191])
+    x = synthetic.activations(T, K, seed=0, n_out=synthetic.n_outliers(K))
+    gamma = synthetic.norm_weights(K, seed=0)
+    wgu = synthetic.weights(2 * F, K, seed=0)
+    wdown = synthetic.weights(K, F, seed=1)
+    dy = synthetic.grad_out(T, K, seed=0)
+    owgu, osgu = oracle.quant_weight(wgu)
+    owd, osd = oracle.quant_weight(wdown)
+    say("mlp fwd+bwd 8B")
+    wgu_q, sgu = u8_to_dev(owgu), f32_to_dev(osgu)
+    wd_q, sd = u8_to_dev(owd), f32_to_dev(osd)
+    saved = fl.fp8_mlp_fwd(bf16_to_dev(x), bf16_to_dev(gamma), wgu_q, sgu, wd_q, sd, eps=eps)
+    wguT, sguT = fl.fp8_weight_transpose(wgu_q, sgu)
+    wdT, sdT = fl.fp8_weight_transpose(wd_q, sd)
+    grads = fl.fp8_mlp_bwd(bf16_to_dev(dy), saved, wguT, sguT, wdT, sdT)
+    # oracle on the sampled rows (every DGrad-path stage is row-local)
+    xs, dys = np.ascontiguousarray(x[rows]), np.ascontiguousarray(dy[rows])
+    xq, sx, _ = oracle.rmsnorm_quant(xs, gamma, eps)
+    gu = oracle.f64_to_bf16(oracle.gemm_fwd(xq, sx, owgu, osgu))
+    g, u = np.ascontiguousarray(gu[:, :F]), np.ascontiguousarray(gu[:, F:])
+    dyq, sdy = oracle.quant_act(dys)
+    dh = oracle.f64_to_bf16(oracle.gemm_dgrad(dyq, sdy, owd, osd))
+    dgu, _ = oracle.swiglu_bwd_bf16(g, u, dh)
+    dguq, sdgu = oracle.quant_act(dgu)
+    dxn = oracle.gemm_dgrad(dguq, sdgu, owgu, osgu)
+    errs = {"dh": rms_rel(bf16_bits_to_f64(host(grads["dh"])[rows]), bf16_bits_to_f64(dh)),
+            "dgu": rms_rel(bf16_bits_to_f64(host(grads["dgu"])[rows]), bf16_bits_to_f64(dgu)),
+            "dxn": rms_rel(bf16_bits_to_f64(host(grads["dxn"])[rows]), dxn)}
+    print("[mlp bwd 8B] rms-relative errors on sampled rows %s" % errs)
+    assert max(errs.values()) <= TOL, errs
+    for k in ("dw_gu", "dw_down"):
+        w = bf16_bits_to_f64(host(grads[k]))
+        assert np.all(np.isfinite(w)) and np.sqrt(np.mean(w * w)) > 0, k
