@@ -124,6 +124,16 @@ def build_step(name, torch, fl, synthetic):
                                                                  out=y),
                    "hbm", gemm_bytes(M, N, K, (N // G) * (K // G)))
             st.dominant = "gemm_fwd"
+        elif name == "decode_unified":
+            st.rotate = max(8, -(-2 * MALL_BYTES // (N * K)))
+            wqs = [fl.fp8_quant_weight(w) for _ in range(st.rotate)]
+            torch.cuda.synchronize()
+            del w
+            st.add("quant_act", lambda i: fl.fp8_quant_act(x, out=(xq, sx)), "hbm", act_quant_bytes(M, K))
+            st.add("gemm_fwd", lambda i: fl.fp8_gemm_fwd_unified(xq, sx, wqs[i % st.rotate][0],
+                                                                  wqs[i % st.rotate][1], out=y),
+                   "hbm", gemm_bytes(M, N, K, (N // G) * (K // G)))
+            st.dominant = "gemm_fwd"
         else:
             wq, sw = empty((N, K), u8), empty((N // G, K // G), f32)
             st.add("quant_act", lambda i: fl.fp8_quant_act(x, out=(xq, sx)), "hbm", act_quant_bytes(M, K))
@@ -532,8 +542,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "large", "backward", "tiny", "producers", "mlp", "mlp_decode",
-                             "mlp_train"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "decode_unified", "prefill", "large", "backward", "tiny", "producers", "mlp",
+                             "mlp_decode", "mlp_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-eager", action="store_true",
                     help="run each kernel of the step eagerly (for rocprofv3 counter passes) and exit")

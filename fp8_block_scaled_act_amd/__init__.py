@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
-    "fp8_gemm_fwd", "fp8_gemm_fwd_packed", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
+    "fp8_gemm_fwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
     "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
@@ -52,6 +52,7 @@ _SYMBOLS = {
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p], ctypes.c_int),
     "fp8_gemm_fwd": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8_gemm_fwd_unified": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_linear_fwd": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 4, ctypes.c_int),
     "fp8_gemm_dgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_gemm_dgrad_t": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
@@ -231,6 +232,22 @@ def fp8_gemm_fwd(xq, sx, wq, sw, out=None, stream=None):
     _expect(y, "y", torch.bfloat16, (M, N))
     _check(lib().fp8_gemm_fwd(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
            "fp8_gemm_fwd")
+    return y
+
+
+def fp8_gemm_fwd_unified(xq, sx, wq, sw, out=None, stream=None):
+    """fp8_gemm_fwd computed by one kernel for every M: a row's output bits do
+    not depend on the rows it is computed with (decode and prefill agree)."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    _expect(xq, "xq", torch.uint8, (M, K))
+    _expect(sx, "sx", torch.float32, (M, K // GROUP))
+    _expect(wq, "wq", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    y = out if out is not None else _empty((M, N), torch.bfloat16, xq)
+    _expect(y, "y", torch.bfloat16, (M, N))
+    _check(lib().fp8_gemm_fwd_unified(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
+           "fp8_gemm_fwd_unified")
     return y
 
 

@@ -313,6 +313,32 @@ fp8lin_status fp8_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq
     return end_launch();
 }
 
+fp8lin_status fp8_gemm_fwd_unified(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                   int64_t M, int64_t N, int64_t K, void* y, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || N % kGroup != 0 || K % kGroup != 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bx, bsx, bw, bsw, by;
+    if (!bytes_of(M, K, 1, &bx) || !bytes_of(M, K / kGroup, 4, &bsx) || !bytes_of(N, K, 1, &bw) ||
+        !bytes_of(N / kGroup, K / kGroup, 4, &bsw))
+        return FP8LIN_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        bx = bsx = bw = bsw = 0;
+    const Buf in[] = {{xq, bx}, {sx, bsx}, {wq, bw}, {sw, bsw}};
+    fp8lin_status s = gemm_common(in, M, N, K, y, &by);
+    if (s != FP8LIN_OK)
+        return s;
+    if (by == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    if (K == 0)
+        fp8lin::launch_fill_zero_bf16(y, M * N, as_stream(stream));
+    else
+        fp8lin::launch_gemm_fwd_unified(xq, sx, wq, sw, M, N, K, y, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_weight_pack(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, void* stream)
 {
     if (N < 0 || K < 0 || N % kGroup != 0 || K % (2 * kGroup) != 0)

@@ -29,6 +29,9 @@ void launch_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void*
 void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st);
 void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                      int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
+// The forward GEMM on one kernel for every M (rows bit-identical across calls).
+void launch_gemm_fwd_unified(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                             int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
 // Decode layout of W (fp8_weight_pack) and the forward GEMM on it
 // (M <= 64, K % 256 == 0, K <= 16384).
 void launch_pack_decode(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, hipStream_t st);

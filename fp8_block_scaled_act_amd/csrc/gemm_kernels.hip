@@ -1291,6 +1291,15 @@ void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, cons
         launch_gemm_nt<Mode::Fwd>(p, st);
 }
 
+void launch_gemm_fwd_unified(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                             int64_t N, int64_t K, void* y, hipStream_t st)
+{
+    // one kernel for every M: each output element is the same MFMA chain over
+    // the same groups in ascending order, whichever tile its row falls in
+    GemmArgs p{xq, sx, wq, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
+    launch_gemm_nt<Mode::Fwd>(p, st);
+}
+
 void launch_pack_decode(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, hipStream_t st)
 {
     const int64_t npieces = N * K / 16;

@@ -318,6 +318,22 @@ fp8lin_status fp8_mlp_fwd(const void* x, const void* gamma, float eps,
                           void* y, void* stream);
 
 /*
+ * Forward GEMM with rollout and training on one kernel: the same product as
+ * fp8_gemm_fwd (same arguments, layouts, errors), computed for every M by
+ * the kernel fp8_gemm_fwd uses above 64 rows.  Jet-RL summary, "Core
+ * architecture": rollout must run the training forward's quantization flow
+ * at the same granularity and precision; this call goes further and makes a
+ * row's output bits independent of the batch it is computed in, so a
+ * decode-sized rollout call and a prefill/training call give bit-identical
+ * rows (fp8_gemm_fwd's decode kernels, used up to 64 rows, sum the groups in
+ * another order and agree with it only within the accuracy metric).  It is
+ * slower than fp8_gemm_fwd for M <= 64.
+ */
+fp8lin_status fp8_gemm_fwd_unified(const uint8_t* xq, const float* sx,
+                                   const uint8_t* wq, const float* sw,
+                                   int64_t M, int64_t N, int64_t K, void* y, void* stream);
+
+/*
  * DGrad GEMM (NN):  dX = dY W, contracted over W's row dimension N.
  * Jet-RL summary, "Quantization scheme": the backward DGrad GEMM runs in FP8.
  *   dX[t,k] = sum_g sdy[t][g] * sw[g][k/128] * sum_{n in g} dec(dyq[t,n]) dec(wq[n,k])

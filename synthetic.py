@@ -111,6 +111,9 @@ WORKLOADS = {
                      "forward quantized linear, X[128,1024] W[1024,1024]"),
     "decode": Workload("decode", "forward", 64, 14336, 4096, n_outliers(4096),
                        "8B-shaped MLP up-proj decode step, X[64,4096] W[14336,4096] pre-quantized"),
+    "decode_unified": Workload("decode_unified", "forward", 64, 14336, 4096, n_outliers(4096),
+                               "8B-shaped MLP up-proj decode step on the unified kernel (rows bit-identical to "
+                               "training-sized calls), X[64,4096] W[14336,4096] pre-quantized"),
     "prefill": Workload("prefill", "forward", 8192, 18944, 3584, n_outliers(3584),
                         "7B-shaped MLP prefill/actor forward, X[8192,3584] W[18944,3584]"),
     "backward": Workload("backward", "backward", 8192, 14336, 4096, n_outliers(4096),

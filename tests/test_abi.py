@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
               "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
               "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
-              "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8_gemm_fwd_unified", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -209,6 +209,17 @@ def test_swiglu_quant_validation(L):
     assert L.fp8_swiglu_quant(A, A + 256, 512, 4, 256, C, D, s0) == DEVICE    # halves of one tensor
     assert L.fp8_swiglu_quant(None, None, 256, 0, 256, None, None, s0) == OK
     assert L.fp8_swiglu_quant(A, B, 256, 4, 256, C, D, s0) == DEVICE
+
+
+@fake_ptrs
+def test_gemm_fwd_unified_validation(L):
+    assert L.fp8_gemm_fwd_unified(A, B, C, D, 4, 100, 128, E, s0) == SHAPE
+    assert L.fp8_gemm_fwd_unified(A, B, C, D, 4, 128, 100, E, s0) == SHAPE
+    assert L.fp8_gemm_fwd_unified(A, B, None, D, 4, 128, 128, E, s0) == NULL
+    assert L.fp8_gemm_fwd_unified(A, B, C, D, 4, 128, 128, C, s0) == ALIAS
+    assert L.fp8_gemm_fwd_unified(A, B, C, D, 4, 128, 128, E + 2, s0) == ALIGN
+    assert L.fp8_gemm_fwd_unified(None, None, None, None, 0, 128, 128, None, s0) == OK
+    assert L.fp8_gemm_fwd_unified(A, B, C, D, 4, 128, 128, E, s0) == DEVICE
 
 
 @fake_ptrs

@@ -226,6 +226,24 @@ def test_fwd_rows_independent_of_batch():
     assert oracle.gemm_metric(bf16_bits_to_f64(y_64), bf16_bits_to_f64(y_all[128:192])) <= TOL
 
 
+def test_fwd_unified_rows_bitwise_across_batch_sizes():
+    """fp8_gemm_fwd_unified: every row's bits are the same whether it is
+    computed alone (rollout decode), in a decode-sized batch or in a large
+    training batch, and equal to fp8_gemm_fwd's above 64 rows; the result meets
+    the accuracy metric against the oracle."""
+    M, N, K = 600, 512, 1536
+    xq, sx = codes_scales((M, K), (M, K // G), 5, 13)
+    wq, sw = codes_scales((N, K), (N // G, K // G), 6, 14)
+    dw, dsw = u8_to_dev(wq), f32_to_dev(sw)
+    run = lambda f, a, b: host(f(u8_to_dev(xq[a:b]), f32_to_dev(sx[a:b]), dw, dsw))
+    say("gemm_fwd_unified batch invariance")
+    y_all = run(fl.fp8_gemm_fwd, 0, M)                 # > 64 rows: the large kernel
+    for a, b in ((0, M), (0, 1), (37, 38), (100, 107), (130, 194), (599, 600), (200, 265), (250, 600)):
+        assert np.array_equal(run(fl.fp8_gemm_fwd_unified, a, b), y_all[a:b]), (a, b)
+    check_metric(run(fl.fp8_gemm_fwd_unified, 130, 194), oracle.gemm_fwd(xq[130:194], sx[130:194], wq, sw),
+                 "unified decode rows")
+
+
 @pytest.mark.parametrize("kind,M,N,K", [("fwd", 64, 14336, 4096), ("fwd", 300, 1024, 1024),
                                         ("dgrad", 300, 1024, 512), ("wgrad", 512, 384, 1024)])
 def test_gemm_deterministic(kind, M, N, K):
