@@ -42,11 +42,13 @@ __device__ __forceinline__ double readlane_f64(double v, int lane)
     return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+// Two fp32 -> two bf16 (low half = lo), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950 (denormals kept, as the kernels' fp32 mode).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // fp64 -> bf16 bits with one rounding to nearest even (finite inputs).
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
         for (int j = 0; j < 4; ++j) {
             const float lo = (bf16_lo(xw[j]) * rs) * bf16_lo(gg[j]);
             const float hi = (bf16_hi(xw[j]) * rs) * bf16_hi(gg[j]);
-            yw[j] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+            yw[j] = pack_bf16x2(lo, hi);
         }
         float scale;
         const uint2 c = quantize_group16(make_uint4(yw[0], yw[1], yw[2], yw[3]), scale);
@@ -219,13 +221,15 @@ __device__ __forceinline__ uint32_t swiglu_bf16_f64(float g, float u)
     return f64_to_bf16_rne((gd / (1.0 + exp(-gd))) * ud);
 }
 
-__device__ __forceinline__ uint32_t swiglu_bf16_f32(float g, float u, bool& redo)
+// The fp32 value (rounded to BF16 by the caller) and whether it must be
+// evaluated again in fp64.
+__device__ __forceinline__ float swiglu_f32(float g, float u, bool& redo)
 {
     const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
     const float v = (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
     const uint32_t b = __float_as_uint(v);
     redo = ((b - 0x7E00u) & 0xFFFFu) <= 0x400u || __builtin_fabsf(g) >= 64.0f;
-    return f32_to_bf16_rne(v);
+    return v;
 }
 
 // The 8 BF16 results of one lane's 16-byte chunks of gate and up.
@@ -238,9 +242,9 @@ __device__ __forceinline__ uint4 swiglu8(uint4 gv, uint4 uv)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         bool r0, r1;
-        const uint32_t h0 = swiglu_bf16_f32(bf16_lo(gw[j]), bf16_lo(uw[j]), r0);
-        const uint32_t h1 = swiglu_bf16_f32(bf16_hi(gw[j]), bf16_hi(uw[j]), r1);
-        hw[j] = h0 | (h1 << 16);
+        const float h0 = swiglu_f32(bf16_lo(gw[j]), bf16_lo(uw[j]), r0);
+        const float h1 = swiglu_f32(bf16_hi(gw[j]), bf16_hi(uw[j]), r1);
+        hw[j] = pack_bf16x2(h0, h1);
         need |= (r0 ? 1u << (2 * j) : 0u) | (r1 ? 2u << (2 * j) : 0u);
     }
     while (need != 0) {                                     // divergent: flagged elements only
