@@ -313,9 +313,59 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
 //
 // BF16 gradients of h = silu(g) u (gradients between operators stay BF16):
 // s = 1 / (1 + exp(-g)), d_up = dh (g s), d_gate = ((dh u) s) (1 + g (1 - s)),
-// each evaluated in fp64 in that order and rounded once to BF16.  A thread
-// owns 8 consecutive columns of one row (16-byte loads of g, u, dh; 16-byte
-// stores of d_gate into dgu[:, :F] and d_up into dgu[:, F:]).
+// each the fp64 evaluation in that order rounded once to BF16.  As in the
+// forward, the kernel first evaluates in fp32 (eps = 2^-24; dh g and dh u are
+// exact products of BF16 values):
+//   e = v_exp_f32(g fl(-log2 e))       rel. error <= 2|g| eps + 4 eps
+//   s = v_rcp_f32(1 + e)               <= 2|g| eps + 7 eps
+//   t = e s  (= 1 - s, no cancellation) <= 4|g| eps + 12 eps
+//   q = g t,  w = 1 + q                 w: <= (|q| / |w|) (4|g| + 13) eps + eps
+//   d_up   = (dh g) s                   <= (2|g| + 8) eps
+//   d_gate = ((dh u) s) w               <= (2|g| + 10 + (|q| / |w|)(4|g| + 13)) eps
+// A relative error of B eps is at most B ulps of the fp32 result, so an
+// output whose fp32 bits lie more than 2B + 2 ulps from a BF16 midpoint
+// rounds as the exact value does.  The others, |g| >= 64 (exponent argument
+// error and exp range), results outside [2^-100, 2^101) (where an
+// intermediate could under- or overflow) and w = 0 are evaluated again in
+// fp64, one flagged element at a time per lane.
+__device__ __forceinline__ void swiglu_bwd_f64(float gf, float uf, float df, uint32_t& bg, uint32_t& bu)
+{
+    const double g = gf, u = uf, d = df;
+    const double sg = 1.0 / (1.0 + exp(-g));
+    bg = f64_to_bf16_rne(((d * u) * sg) * (1.0 + g * (1.0 - sg)));
+    bu = f64_to_bf16_rne(d * (g * sg));
+}
+
+// true when fp32 v may round to a different BF16 than a value within `ulps`
+// ulps of it, or lies outside the range where the bound holds
+__device__ __forceinline__ bool needs_f64(float v, float ulps)
+{
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t low = b & 0xFFFFu;
+    const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
+    const uint32_t ex = (b >> 23) & 0xFFu;
+    const uint32_t lim = (uint32_t)__builtin_amdgcn_fmed3f(2.0f * ulps + 2.0f, 0.0f, 65536.0f);
+    return dist <= lim || ex < 27u || ex > 227u;
+}
+
+__device__ __forceinline__ void swiglu_bwd_f32(float g, float u, float dh, float& vg, float& vu, bool& redo)
+{
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    const float s = __builtin_amdgcn_rcpf(1.0f + e);
+    const float t = e * s;
+    const float q = g * t;
+    const float w = 1.0f + q;
+    vu = (dh * g) * s;
+    vg = ((dh * u) * s) * w;
+    const float ag = __builtin_fabsf(g);
+    const float r = __builtin_fabsf(q) * __builtin_amdgcn_rcpf(__builtin_fabsf(w));   // +inf when w = 0
+    const float bu = 2.0f * ag + 8.0f;
+    const float bg = 2.0f * ag + 10.0f + r * (4.0f * ag + 13.0f);
+    redo = ag >= 64.0f || !(bg < 65536.0f) || needs_f64(vu, bu) || needs_f64(vg, bg);
+}
+
+// A thread owns 8 consecutive columns of one row (16-byte loads of g, u, dh;
+// 16-byte stores of d_gate into dgu[:, :F] and d_up into dgu[:, F:]).
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restrict__ gate,
                                                          const uint16_t* __restrict__ up, int64_t ld,
                                                          const uint16_t* __restrict__ dh, int64_t F,
@@ -331,20 +381,38 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
         const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
         const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
         uint32_t og[4], ou[4];
+        uint32_t need = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t rg[2], ru[2];
+            float vg0, vu0, vg1, vu1;
+            bool r0, r1;
+            swiglu_bwd_f32(bf16_lo(gw[j]), bf16_lo(uw[j]), bf16_lo(dw[j]), vg0, vu0, r0);
+            swiglu_bwd_f32(bf16_hi(gw[j]), bf16_hi(uw[j]), bf16_hi(dw[j]), vg1, vu1, r1);
+            og[j] = pack_bf16x2(vg0, vg1);
+            ou[j] = pack_bf16x2(vu0, vu1);
+            need |= (r0 ? 1u << (2 * j) : 0u) | (r1 ? 2u << (2 * j) : 0u);
+        }
+        while (need != 0) {                                 // divergent: flagged elements only
+            const int k = __builtin_ctz(need);
+            need &= need - 1;
+            uint32_t gs = 0, us = 0, ds = 0;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const double g = h ? bf16_hi(gw[j]) : bf16_lo(gw[j]);
-                const double u = h ? bf16_hi(uw[j]) : bf16_lo(uw[j]);
-                const double d = h ? bf16_hi(dw[j]) : bf16_lo(dw[j]);
-                const double sg = 1.0 / (1.0 + exp(-g));
-                rg[h] = f64_to_bf16_rne(((d * u) * sg) * (1.0 + g * (1.0 - sg)));
-                ru[h] = f64_to_bf16_rne(d * (g * sg));
-            }
-            og[j] = rg[0] | (rg[1] << 16);
-            ou[j] = ru[0] | (ru[1] << 16);
+            for (int j = 0; j < 4; ++j)
+                if ((k >> 1) == j) {
+                    gs = gw[j];
+                    us = uw[j];
+                    ds = dw[j];
+                }
+            const bool hi = k & 1;
+            uint32_t bg, bu;
+            swiglu_bwd_f64(hi ? bf16_hi(gs) : bf16_lo(gs), hi ? bf16_hi(us) : bf16_lo(us),
+                           hi ? bf16_hi(ds) : bf16_lo(ds), bg, bu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((k >> 1) == j) {
+                    og[j] = hi ? ((og[j] & 0xFFFFu) | (bg << 16)) : ((og[j] & 0xFFFF0000u) | bg);
+                    ou[j] = hi ? ((ou[j] & 0xFFFFu) | (bu << 16)) : ((ou[j] & 0xFFFF0000u) | bu);
+                }
         }
         uint16_t* row = dgu + m * 2 * F + c;
         *reinterpret_cast<uint4*>(row) = make_uint4(og[0], og[1], og[2], og[3]);
