@@ -167,8 +167,13 @@ def build_step(name, torch, fl, synthetic):
         gu = empty((T, 2 * F), bf)
         hq, sh = empty((T, F), u8), empty((T, F // G), f32)
         y = empty((T, K), bf)
-        gemm = fl.fp8_gemm_fwd_packed if decode else fl.fp8_gemm_fwd
         kind = "hbm" if decode else "mfma"
+        if decode:                                  # split over K where the weight has few columns
+            wsp = torch.empty((max(max(fl.fp8_gemm_fwd_packed_splitk_workspace(T, n, k)
+                                       for n, k in ((2 * F, K), (K, F))) // 4, 1),), dtype=f32, device=dev)
+            gemm = lambda a, sa, b, sb, out: fl.fp8_gemm_fwd_packed_splitk(a, sa, b, sb, workspace=wsp, out=out)
+        else:
+            gemm = fl.fp8_gemm_fwd
         st.add("rmsnorm_quant", lambda i: fl.fp8_rmsnorm_quant(x, gamma, 1e-6, out=(xq, sx, rstd)), "hbm",
                act_quant_bytes(T, K) + 4 * T + 2 * K)
         st.add("gemm_gate_up", lambda i: gemm(xq, sx, ws[i % st.rotate][0], ws[i % st.rotate][1], out=gu), kind,

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
-    "fp8_gemm_fwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
+    "fp8_gemm_fwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed",
+    "fp8_gemm_fwd_packed_splitk", "fp8_gemm_fwd_packed_splitk_workspace", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
     "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
@@ -52,6 +53,9 @@ _SYMBOLS = {
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p], ctypes.c_int),
     "fp8_gemm_fwd": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
+    "fp8_gemm_fwd_packed_splitk": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2 +
+                                   [ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
+    "fp8_gemm_fwd_packed_splitk_workspace": ([ctypes.c_int64] * 3, ctypes.c_int64),
     "fp8_gemm_fwd_unified": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_linear_fwd": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 4, ctypes.c_int),
     "fp8_gemm_dgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
@@ -232,6 +236,37 @@ def fp8_gemm_fwd(xq, sx, wq, sw, out=None, stream=None):
     _expect(y, "y", torch.bfloat16, (M, N))
     _check(lib().fp8_gemm_fwd(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
            "fp8_gemm_fwd")
+    return y
+
+
+def fp8_gemm_fwd_packed_splitk_workspace(M: int, N: int, K: int) -> int:
+    """Workspace bytes fp8_gemm_fwd_packed_splitk needs for this shape (0: none)."""
+    n = lib().fp8_gemm_fwd_packed_splitk_workspace(M, N, K)
+    if n < 0:
+        raise Fp8LinError(2, "fp8_gemm_fwd_packed_splitk_workspace")
+    return n
+
+
+def fp8_gemm_fwd_packed_splitk(xq, sx, wqp, sw, workspace=None, out=None, stream=None):
+    """fp8_gemm_fwd_packed split over K for few output columns.  workspace: a
+    float32 CUDA tensor of at least fp8_gemm_fwd_packed_splitk_workspace bytes
+    (allocated here when None)."""
+    M, K = xq.shape
+    N = wqp.shape[0]
+    _expect(xq, "xq", torch.uint8, (M, K))
+    _expect(sx, "sx", torch.float32, (M, K // GROUP))
+    _expect(wqp, "wqp", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    need = fp8_gemm_fwd_packed_splitk_workspace(M, N, K)
+    if workspace is None:
+        workspace = _empty((max(need // 4, 1),), torch.float32, xq)
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous float32 tensor")
+    y = out if out is not None else _empty((M, N), torch.bfloat16, xq)
+    _expect(y, "y", torch.bfloat16, (M, N))
+    _check(lib().fp8_gemm_fwd_packed_splitk(_ptr(xq), _ptr(sx), _ptr(wqp), _ptr(sw), M, N, K, _ptr(y),
+                                            _ptr(workspace), workspace.numel() * 4, _stream(stream)),
+           "fp8_gemm_fwd_packed_splitk")
     return y
 
 

@@ -385,6 +385,47 @@ fp8lin_status fp8_gemm_fwd_packed(const uint8_t* xq, const float* sx, const uint
     return end_launch();
 }
 
+int64_t fp8_gemm_fwd_packed_splitk_workspace(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || M > 64 || N < 0 || K < 0 || N % kGroup != 0 || K % (2 * kGroup) != 0 || K > 128 * kGroup)
+        return -1;
+    if (M == 0 || N == 0 || K == 0)
+        return 0;
+    const int64_t S = fp8lin::splitk_splits(N, K);
+    return S > 1 ? S * M * N * 4 : 0;
+}
+
+fp8lin_status fp8_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx, const uint8_t* wqp, const float* sw,
+                                         int64_t M, int64_t N, int64_t K, void* y, float* workspace,
+                                         int64_t workspace_bytes, void* stream)
+{
+    const int64_t need = fp8_gemm_fwd_packed_splitk_workspace(M, N, K);
+    if (need < 0)
+        return FP8LIN_ERR_SHAPE;
+    if (workspace_bytes < need)
+        return FP8LIN_ERR_ARG;
+    int64_t bx, bsx, bw, bsw, by;
+    if (!bytes_of(M, K, 1, &bx) || !bytes_of(M, K / kGroup, 4, &bsx) || !bytes_of(N, K, 1, &bw) ||
+        !bytes_of(N / kGroup, K / kGroup, 4, &bsw) || !bytes_of(M, N, 2, &by))
+        return FP8LIN_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        bx = bsx = bw = bsw = 0;
+    const Buf in[] = {{xq, bx}, {sx, bsx}, {wqp, bw}, {sw, bsw}};
+    const Buf out[] = {{y, by}, {workspace, need}};
+    fp8lin_status s = check_buffers(in, 4, out, 2);
+    if (s != FP8LIN_OK)
+        return s;
+    if (by == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    if (K == 0)
+        fp8lin::launch_fill_zero_bf16(y, M * N, as_stream(stream));
+    else
+        fp8lin::launch_gemm_fwd_packed_splitk(xq, sx, wqp, sw, M, N, K, y, workspace, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_linear_fwd(const void* x, const uint8_t* wq, const float* sw, int64_t M, int64_t N, int64_t K,
                              uint8_t* xq, float* sx, void* y, void* stream)
 {

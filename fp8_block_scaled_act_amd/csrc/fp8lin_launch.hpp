@@ -37,6 +37,11 @@ void launch_gemm_fwd_unified(const uint8_t* xq, const float* sx, const uint8_t* 
 void launch_pack_decode(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, hipStream_t st);
 void launch_gemm_fwd_packed(const uint8_t* xq, const float* sx, const uint8_t* wqp, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
+// Split-K variant for few output columns: S = splitk_splits(N, K) workgroups
+// per 64-column block, fp32 partials in ws [S][M][N] (unused when S == 1).
+int64_t splitk_splits(int64_t N, int64_t K);
+void launch_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx, const uint8_t* wqp, const float* sw,
+                                   int64_t M, int64_t N, int64_t K, void* y, float* ws, hipStream_t st);
 void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
                        int64_t T, int64_t N, int64_t K, void* dx, hipStream_t st);
 void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,

@@ -969,6 +969,160 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_kernel(const GemmA
     }
 }
 
+// ------------------------------------ decode on the packed W, split over K
+//
+// For weights with few output columns (N / 64 workgroups leave most CUs
+// idle, e.g. the MLP down projection, N = 4096) the chunks of the contraction
+// are divided over S workgroups per 64-column block (blockIdx.y = split).
+// Each computes the packed kernel's product over its chunk range [c0, c1)
+// (same roles, same per-chunk arithmetic, the four wave partials added in the
+// same fixed order) and writes that fp32 64x64 partial tile to the caller's
+// workspace, [S][M][N]; splitk_reduce_kernel then adds the S partials in
+// ascending split order and rounds to BF16.  Deterministic, rows independent
+// of the other rows of the call; not bit-identical to the unsplit kernels
+// (the groups are added in another association).
+template <int GM>
+__global__ __launch_bounds__(576) void gemm_fwd_decode_packed_splitk_kernel(const GemmArgs p, float* ws,
+                                                                            int64_t per_split)
+{
+    using namespace dec;
+    constexpr int WDX = 4;
+    static_assert(WDX * WCH >= 3 * 2 * 2 * 16 * 64 * 4, "partial sums fit in the X ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_x[WDX][WCH];
+    __shared__ __attribute__((aligned(16))) float lds_ps[64 * (GM + 1)];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t G = p.Kc / kGroup, nch = G / CH;
+    const int GP = (int)G | 1;
+    const int64_t n0 = (int64_t)blockIdx.x * 64;
+    const int64_t c0 = (int64_t)blockIdx.y * per_split;
+    const int64_t c1 = c0 + per_split < nch ? c0 + per_split : nch;
+    const int64_t nloc = c1 - c0;                  // >= 1: the launcher sizes the splits
+
+    if (wave < 8) {
+        decode_scale_table(p, n0, G, GP, tid, lds_ps);
+        const u32x4* wsrc = reinterpret_cast<const u32x4*>(p.b) + packed_piece(blockIdx.x, nch, 0, wave, 0, lane);
+        u32x4 wreg[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            wreg[q] = __builtin_nontemporal_load(wsrc + c0 * (8 * 2 * 64) + q * 64);
+        const int ct = wave & 1, kp = (wave >> 1) & 1, kq = wave >> 2;
+        const int m = lane & 31, kh = lane >> 5;
+        v16f acc[2];
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[xt][r] = 0.f;
+        __syncthreads();                           // local chunk 0 of X landed, table built
+        for (int64_t lc = 0; lc < nloc; ++lc) {
+            const int64_t c = c0 + lc;
+            const uint8_t* xl = lds_x[lc % WDX];
+            u32x4 xv[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt)
+                    xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
+            v8h wlo[2], whi[2];
+            // convert this chunk's W fragments before the next chunk is
+            // loaded into their registers
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                wlo[q] = cvt8(wreg[q].x, wreg[q].y);
+                whi[q] = cvt8(wreg[q].z, wreg[q].w);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                const int64_t cn = c + 1 < c1 ? c + 1 : c;   // last chunk: a harmless re-read
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    wreg[q] = __builtin_nontemporal_load(wsrc + cn * (8 * 2 * 64) + q * 64);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            v16f tmp[2];
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    tmp[xt][r] = 0.f;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt) {
+                    const v8h xlo = cvt8(xv[xt][q].x, xv[xt][q].y), xhi = cvt8(xv[xt][q].z, xv[xt][q].w);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wlo[q], xlo, tmp[xt], 0, 0, 0);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(whi[q], xhi, tmp[xt], 0, 0, 0);
+                }
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt) {
+                const float sc = lds_ps[(32 * xt + m) * GP + c * CH + kp];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[xt][r] = fmaf(tmp[xt][r], sc, acc[xt][r]);
+            }
+            __syncthreads();                       // chunk drained, the next one landed
+        }
+        __syncthreads();                           // the loader drained: the X ring is idle
+        // the four (kp, kq) partials in the fixed order of decode_reduce_store,
+        // then the fp32 tile to ws[split]
+        float* red = reinterpret_cast<float*>(&lds_x[0][0]);
+        const int part = kp * 2 + kq;
+        if (part != 0) {
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    red[(((part - 1) * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane] = acc[xt][r];
+        }
+        __syncthreads();
+        if (part == 0) {
+            float* dst = ws + (int64_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt) {
+                const int64_t row = 32 * xt + m;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int pp = 0; pp < 3; ++pp)
+                        acc[xt][r] += red[((pp * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane];
+                if (row < p.M) {
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4)
+                        *reinterpret_cast<float4*>(dst + row * p.N + n0 + 32 * ct + 8 * a4 + 4 * kh) =
+                            make_float4(acc[xt][4 * a4], acc[xt][4 * a4 + 1], acc[xt][4 * a4 + 2],
+                                        acc[xt][4 * a4 + 3]);
+                }
+            }
+        }
+    } else {
+        stream_operand<WDX>(p.a + c0 * (CH * kGroup), p.M, 0, p.Kc, nloc, (uint32_t)(uintptr_t)&lds_x[0][0],
+                            lane);
+    }
+}
+
+// y[m][n] = bf16(sum over splits, ascending, of ws[split][m][n]); 4 columns
+// per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t mn,
+                                                            uint16_t* __restrict__ y)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= mn)
+        return;
+    float4 a = *reinterpret_cast<const float4*>(ws + i);
+    for (int k = 1; k < S; ++k) {
+        const float4 b = *reinterpret_cast<const float4*>(ws + (int64_t)k * mn + i);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    *reinterpret_cast<u32x2*>(y + i) =
+        u32x2{(uint32_t)f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16),
+              (uint32_t)f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16)};
+}
+
 // W codes [N][K] -> the decode layout above, one 16-byte piece per thread
 // (stores coalesced, loads gathered; done once per weight update).
 __global__ __launch_bounds__(256) void pack_decode_kernel(const uint8_t* __restrict__ wq, int64_t K,
@@ -1298,6 +1452,45 @@ void launch_gemm_fwd_unified(const uint8_t* xq, const float* sx, const uint8_t* 
     // the same groups in ascending order, whichever tile its row falls in
     GemmArgs p{xq, sx, wq, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
     launch_gemm_nt<Mode::Fwd>(p, st);
+}
+
+// Splits per 64-column block for the split-K decode GEMM: none when the
+// 64-column blocks already fill half the CUs, else enough workgroups to cover
+// the 256 CUs with at least two chunks (512 columns of K) per split.
+int64_t splitk_splits(int64_t N, int64_t K)
+{
+    const int64_t blocks = N / 64, nch = K / (dec::CH * kGroup);
+    if (blocks >= 128)
+        return 1;                                  // at least half the CUs busy: no split
+    int64_t s = blocks > 0 ? (256 + blocks - 1) / blocks : 1;
+    if (s > nch / 2)
+        s = nch / 2;
+    if (s < 1)
+        s = 1;
+    // equal chunk ranges, none empty
+    const int64_t per = (nch + s - 1) / s;
+    return (nch + per - 1) / per;
+}
+
+void launch_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx, const uint8_t* wqp, const float* sw,
+                                   int64_t M, int64_t N, int64_t K, void* y, float* ws, hipStream_t st)
+{
+    const int64_t S = splitk_splits(N, K);
+    if (S <= 1) {
+        launch_gemm_fwd_packed(xq, sx, wqp, sw, M, N, K, y, st);
+        return;
+    }
+    GemmArgs p{xq, sx, wqp, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
+    const int64_t nch = K / (dec::CH * kGroup);
+    const int64_t per = (nch + S - 1) / S;
+    const dim3 grid((unsigned)(N / 64), (unsigned)S);
+    if (K / kGroup <= 64)
+        gemm_fwd_decode_packed_splitk_kernel<64><<<grid, 576, 0, st>>>(p, ws, per);
+    else
+        gemm_fwd_decode_packed_splitk_kernel<128><<<grid, 576, 0, st>>>(p, ws, per);
+    const int64_t mn = M * N;
+    splitk_reduce_kernel<<<(unsigned)((mn / 4 + 255) / 256), 256, 0, st>>>(ws, (int)S, mn,
+                                                                          static_cast<uint16_t*>(y));
 }
 
 void launch_pack_decode(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, hipStream_t st)

@@ -318,6 +318,31 @@ fp8lin_status fp8_mlp_fwd(const void* x, const void* gamma, float eps,
                           void* y, void* stream);
 
 /*
+ * Rollout GEMM on the decode layout, split over the contraction for weights
+ * with few output columns (the MLP down projection and attention projections
+ * of a decode step: N / 64 column blocks leave most CUs idle).  Same product,
+ * arguments, layouts and limits as fp8_gemm_fwd_packed (Jet-RL summary,
+ * "Quantization scheme": 1x128 activations, 128x128 weights), plus a
+ * caller-owned device workspace for fp32 partial sums:
+ *   workspace       : float, at least fp8_gemm_fwd_packed_splitk_workspace(M, N, K)
+ *                     bytes (0: may be NULL), 16-byte aligned, not overlapping
+ *                     any argument; its contents on entry are ignored and on
+ *                     return are unspecified.  Calls that share a workspace
+ *                     must be ordered on one stream.
+ * When the weight has at least 128 column blocks (N >= 8192) no split is made
+ * and the result is bit-identical to fp8_gemm_fwd_packed; otherwise the S
+ * partial products (S workgroups per 64-column block) are added in ascending
+ * split order: deterministic, rows independent of the other rows, within the
+ * accuracy metric of fp8_gemm_fwd_packed but not bit-identical to it.
+ * Errors as fp8_gemm_fwd_packed; workspace_bytes too small: FP8LIN_ERR_ARG.
+ */
+int64_t fp8_gemm_fwd_packed_splitk_workspace(int64_t M, int64_t N, int64_t K);   /* -1: invalid shape */
+fp8lin_status fp8_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx,
+                                         const uint8_t* wqp, const float* sw,
+                                         int64_t M, int64_t N, int64_t K, void* y,
+                                         float* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Forward GEMM with rollout and training on one kernel: the same product as
  * fp8_gemm_fwd (same arguments, layouts, errors), computed for every M by
  * the kernel fp8_gemm_fwd uses above 64 rows.  Jet-RL summary, "Core

@@ -22,7 +22,7 @@ HAS_GPU = torch.cuda.is_available()
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(?:fp8lin_status|int|const char\*)\s+(\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(?:fp8lin_status|int64_t|int|const char\*)\s+(\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(L):
     for n in ["fp8_quant_act", "fp8_quant_weight", "fp8_quant_transpose", "fp8_gemm_fwd",
               "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
               "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
-              "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8_gemm_fwd_unified", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed_splitk",
+              "fp8_gemm_fwd_packed_splitk_workspace", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -209,6 +210,26 @@ def test_swiglu_quant_validation(L):
     assert L.fp8_swiglu_quant(A, A + 256, 512, 4, 256, C, D, s0) == DEVICE    # halves of one tensor
     assert L.fp8_swiglu_quant(None, None, 256, 0, 256, None, None, s0) == OK
     assert L.fp8_swiglu_quant(A, B, 256, 4, 256, C, D, s0) == DEVICE
+
+
+def test_splitk_workspace_query(L):
+    assert L.fp8_gemm_fwd_packed_splitk_workspace(65, 4096, 4096) == -1          # M > 64
+    assert L.fp8_gemm_fwd_packed_splitk_workspace(64, 4096, 384) == -1           # K % 256
+    assert L.fp8_gemm_fwd_packed_splitk_workspace(64, 14336, 4096) == 0          # enough columns: no split
+    assert L.fp8_gemm_fwd_packed_splitk_workspace(64, 4096, 14336) == 4 * 64 * 4096 * 4
+    assert L.fp8_gemm_fwd_packed_splitk_workspace(0, 4096, 14336) == 0
+
+
+@fake_ptrs
+def test_splitk_validation(L):
+    need = L.fp8_gemm_fwd_packed_splitk_workspace(64, 4096, 4096)
+    assert need > 0
+    assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 4096, 4096, E, F, need - 1, s0) == ARG
+    assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 65, 4096, 4096, E, F, need, s0) == SHAPE
+    assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 4096, 4096, E, C, need, s0) == ALIAS     # ws over wqp
+    assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 4096, 4096, E, F + 4, need, s0) == ALIGN
+    assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 14336, 4096, E, None, 0, s0) == DEVICE    # no split
+    assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 4096, 4096, E, F, need, s0) == DEVICE
 
 
 @fake_ptrs

@@ -121,6 +121,37 @@ def test_fwd_packed_matches_unpacked(M, N, K):
         check_metric(y, oracle.gemm_fwd(xq, sx, wq, sw), "fwd packed %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 14336), (64, 4096, 4096), (17, 1024, 2048), (1, 256, 4096),
+                                   (64, 4096, 3584), (33, 512, 5120), (64, 14336, 4096)])
+def test_fwd_packed_splitk(M, N, K):
+    """The split-K decode GEMM: within the tolerance of the oracle (the 8B down
+    projection 64x4096x14336 included, split ranges of unequal length at
+    K = 3584), deterministic, rows bit-identical across batch sizes, and
+    bit-identical to the unsplit kernel when no split is made (N >= 8192)."""
+    xq, sx = codes_scales((M, K), (M, K // G), M * 7 + K, 64)
+    wq, sw = codes_scales((N, K), (N // G, K // G), N * 5 + K, 65)
+    say("gemm_fwd_packed_splitk", M, N, K)
+    xd, sxd, wd, swd = u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw)
+    wp = fl.fp8_weight_pack(wd)
+    need = fl.fp8_gemm_fwd_packed_splitk_workspace(M, N, K)
+    ws = torch.full((max(need // 4, 1),), float("nan"), dtype=torch.float32, device=DEV)   # contents ignored
+    y = host(fl.fp8_gemm_fwd_packed_splitk(xd, sxd, wp, swd, workspace=ws))
+    assert np.array_equal(y, host(fl.fp8_gemm_fwd_packed_splitk(xd, sxd, wp, swd, workspace=ws)))
+    if need == 0:
+        assert np.array_equal(y, host(fl.fp8_gemm_fwd_packed(xd, sxd, wp, swd)))
+    rows = slice(M // 3, M // 3 + 1)
+    y1 = host(fl.fp8_gemm_fwd_packed_splitk(xd[rows].contiguous(), sxd[rows].contiguous(), wp, swd))
+    assert np.array_equal(y1, y[rows])
+    if N * K <= 4096 * 14336:
+        check_metric(y, oracle.gemm_fwd(xq, sx, wq, sw), "fwd packed split-K %dx%dx%d" % (M, N, K))
+    if need > 0:
+        with pytest.raises(fl.Fp8LinError, match="FP8LIN_ERR_ARG"):
+            fl._check(fl.lib().fp8_gemm_fwd_packed_splitk(
+                fl._ptr(xd), fl._ptr(sxd), fl._ptr(wp), fl._ptr(swd), M, N, K, fl._ptr(torch.empty_like(
+                    torch.zeros((M, N), dtype=torch.bfloat16, device=DEV))), fl._ptr(ws), need - 4,
+                fl._stream(None)), "splitk")
+
+
 def test_fwd_one_hot_every_code():
     """Pins MFMA operand decoding and the fragment/output layouts: W holds every
     finite code once in column 0 of its group; X is one-hot at that column."""
