@@ -201,7 +201,7 @@ def build_step(name, torch, fl, synthetic):
         gu, hq, sh, y = empty((T, 2 * F), bf), empty((T, F), u8), empty((T, F // G), f32), empty((T, K), bf)
         dyTq, sdyT, dyq, sdy = empty((K, T), u8), empty((K, T // G), f32), empty((T, K), u8), empty((T, K // G), f32)
         hTq, shT = empty((F, T), u8), empty((F, T // G), f32)
-        dwd, dh, dgu = empty((K, F), bf), empty((T, F), bf), empty((T, 2 * F), bf)
+        dwd, dh = empty((K, F), bf), empty((T, F), bf)
         dguTq, sdguT = empty((2 * F, T), u8), empty((2 * F, T // G), f32)
         dguq, sdgu = empty((T, 2 * F), u8), empty((T, 2 * F // G), f32)
         xTq, sxT = empty((K, T), u8), empty((K, T // G), f32)
@@ -220,10 +220,9 @@ def build_step(name, torch, fl, synthetic):
                requant(T, F))
         st.add("gemm_wgrad_down", lambda i: fl.fp8_gemm_wgrad(dyTq, sdyT, hTq, shT, out=dwd), "mfma", 2 * T * K * F)
         st.add("gemm_dgrad_down", lambda i: fl.fp8_gemm_dgrad_t(dyq, sdy, wdT, sdT, out=dh), "mfma", 2 * T * K * F)
-        st.add("swiglu_bwd", lambda i: fl.fp8_swiglu_bwd(gu[:, :F], gu[:, F:], dh, out=dgu), "hbm",
-               3 * T * F * 2 + 2 * T * F * 2)
-        st.add("quant_transpose_dual_dGU",
-               lambda i: fl.fp8_quant_transpose(dgu, dual=True, out=(dguTq, sdguT, dguq, sdgu)), "hbm", dual(T, 2 * F))
+        st.add("swiglu_bwd_quant",
+               lambda i: fl.fp8_swiglu_bwd_quant(gu[:, :F], gu[:, F:], dh, out=(dguTq, sdguT, dguq, sdgu)), "hbm",
+               3 * T * F * 2 + 2 * (2 * T * F) + (2 * F * (T // G) + T * (2 * F // G)) * 4)
         st.add("quant_transpose_fp8_X", lambda i: fl.fp8_quant_transpose(xq, sx, out=(xTq, sxT, None, None)), "hbm",
                requant(T, K))
         st.add("gemm_wgrad_gate_up", lambda i: fl.fp8_gemm_wgrad(dguTq, sdguT, xTq, sxT, out=dwgu), "mfma",
@@ -429,7 +428,7 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
 KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes from
     "quant_act": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "quant_weight": ("quant_kernels.hip", "fp8lin_device.hpp"),
-    "quant_transpose_dual_dY": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "quant_transpose_dual_dY": ("quant_kernels.hip", "quant_tile.hpp", "fp8lin_device.hpp"),
     "quant_transpose_fp8_X": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "gemm_fwd": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_dgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
@@ -442,6 +441,7 @@ KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes f
     "quant_transpose_fp8_H": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "quant_transpose_dual_dGU": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_bwd": ("producer_kernels.hip", "fp8lin_device.hpp"),
+    "swiglu_bwd_quant": ("producer_kernels.hip", "quant_tile.hpp", "fp8lin_device.hpp"),
     "gemm_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "rmsnorm_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
@@ -464,6 +464,7 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "quant_transpose_fp8_H": None,
     "quant_transpose_dual_dGU": None,
     "swiglu_bwd": "swiglu_bwd_kernel",
+    "swiglu_bwd_quant": "swiglu_bwd_quant_kernel",
     "gemm_gate_up": None,       # same kernel as gemm_down: counters cannot tell them apart
     "gemm_down": None,
     "rmsnorm_quant": "rmsnorm_quant_kernel",

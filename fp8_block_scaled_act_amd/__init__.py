@@ -23,7 +23,7 @@ __all__ = [
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
     "fp8_gemm_fwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed",
     "fp8_gemm_fwd_packed_splitk", "fp8_gemm_fwd_packed_splitk_workspace", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
-    "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_mlp_fwd", "fp8_mlp_bwd",
+    "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_swiglu_bwd_quant", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -67,6 +67,8 @@ _SYMBOLS = {
                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "fp8_swiglu_bwd": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "fp8_swiglu_bwd_quant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                              ctypes.c_int64] + [ctypes.c_void_p] * 5, ctypes.c_int),
     "fp8_mlp_fwd": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float] + [ctypes.c_void_p] * 4 +
                     [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 8, ctypes.c_int),
     "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
@@ -397,6 +399,36 @@ def fp8_swiglu_bwd(gate, up, dh, out=None, stream=None):
     return dgu
 
 
+def fp8_swiglu_bwd_quant(gate, up, dh, out=None, stream=None):
+    """SwiGLU backward fused with the dual FP8 quantization of its result:
+    returns (dguTq u8 [2F,T], sdguT f32 [2F,T/128], dguq u8 [T,2F], sdgu f32
+    [T,2F/128]) -- the order of fp8_quant_transpose(..., dual=True)."""
+    if gate.shape != up.shape or gate.dim() != 2:
+        raise ValueError("gate and up must be 2-D tensors of one shape")
+    T, F = gate.shape
+    _expect(dh, "dh", torch.bfloat16, (T, F))
+    for t, name in ((gate, "gate"), (up, "up")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be torch.bfloat16" % name)
+        if T and F and t.stride(1) != 1:
+            raise ValueError("%s must have unit column stride" % name)
+    ld = gate.stride(0) if T > 1 else F
+    if T > 1 and up.stride(0) != ld:
+        raise ValueError("gate and up must have the same row stride")
+    if out is None:
+        qT, sT = _empty((2 * F, T), torch.uint8, dh), _empty((2 * F, T // GROUP), torch.float32, dh)
+        q, s = _empty((T, 2 * F), torch.uint8, dh), _empty((T, 2 * F // GROUP), torch.float32, dh)
+    else:
+        qT, sT, q, s = out
+    _expect(qT, "dguTq", torch.uint8, (2 * F, T))
+    _expect(sT, "sdguT", torch.float32, (2 * F, T // GROUP))
+    _expect(q, "dguq", torch.uint8, (T, 2 * F))
+    _expect(s, "sdgu", torch.float32, (T, 2 * F // GROUP))
+    _check(lib().fp8_swiglu_bwd_quant(_ptr(gate), _ptr(up), ld, _ptr(dh), T, F, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT),
+                                      _stream(stream)), "fp8_swiglu_bwd_quant")
+    return qT, sT, q, s
+
+
 def fp8_mlp_fwd(x, gamma, wgu, sgu, wdown, sdown, eps: float = 1e-6, out=None, rstd: bool = True, stream=None):
     """Forward pass of an FP8 MLP block: RMSNorm -> gate/up GEMM -> SwiGLU -> down GEMM.
 
@@ -443,8 +475,8 @@ def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, stream=None):
       fp8_quant_transpose(hq, sh)             -> H^T q        (saved FP8 SwiGLU output)
       fp8_gemm_wgrad(dY^T q, H^T q)           -> dw_down [K,F]
       fp8_gemm_dgrad_t(dYq, W_down^T)         -> dh [T,F]
-      fp8_swiglu_bwd(gate, up, dh)            -> dgu [T,2F]   (BF16)
-      fp8_quant_transpose(dgu, dual)          -> dGUq, dGU^T q
+      fp8_swiglu_bwd_quant(gate, up, dh)      -> dGUq, dGU^T q (SwiGLU backward fused with the
+                                                 dual quantization of its BF16 result)
       fp8_quant_transpose(xq, sx)             -> X^T q        (saved FP8 block input)
       fp8_gemm_wgrad(dGU^T q, X^T q)          -> dw_gu [2F,K]
       fp8_gemm_dgrad_t(dGUq, W_gu^T)          -> dxn [T,K]    (gradient of the RMSNorm output)
@@ -452,7 +484,7 @@ def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, stream=None):
     dy bf16 [T,K]; saved is the dict returned by fp8_mlp_fwd; wguT/sguT and
     wdT/sdT are the transposed weight copies (fp8_weight_transpose of the
     fused gate/up and down weights).  T % 128 == 0 (WGrad groups run along T).
-    Returns dict(dxn, dw_gu, dw_down, dh, dgu)."""
+    Returns dict(dxn, dw_gu, dw_down, dh)."""
     T, K = dy.shape
     F = saved["hq"].shape[1]
     st = stream
@@ -461,12 +493,11 @@ def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, stream=None):
     dw_down = fp8_gemm_wgrad(dyTq, sdyT, hTq, shT, stream=st)
     dh = fp8_gemm_dgrad_t(dyq, sdy, wdT, sdT, stream=st)
     gu = saved["gu"]
-    dgu = fp8_swiglu_bwd(gu[:, :F], gu[:, F:], dh, stream=st)
-    dguTq, sguT_, dguq, sdgu = fp8_quant_transpose(dgu, dual=True, stream=st)
+    dguTq, sguT_, dguq, sdgu = fp8_swiglu_bwd_quant(gu[:, :F], gu[:, F:], dh, stream=st)
     xTq, sxT = fp8_quant_transpose(saved["xq"], saved["sx"], stream=st)
     dw_gu = fp8_gemm_wgrad(dguTq, sguT_, xTq, sxT, stream=st)
     dxn = fp8_gemm_dgrad_t(dguq, sdgu, wguT, sguT, stream=st)
-    return {"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh, "dgu": dgu}
+    return {"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh}
 
 
 def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):

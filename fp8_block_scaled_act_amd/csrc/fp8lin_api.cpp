@@ -540,6 +540,33 @@ fp8lin_status fp8_swiglu_bwd(const void* gate, const void* up, int64_t ld, const
     return end_launch();
 }
 
+fp8lin_status fp8_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const void* dh, int64_t T, int64_t F,
+                                   uint8_t* dguq, float* sdgu, uint8_t* dguTq, float* sdguT, void* stream)
+{
+    if (T < 0 || F < 0 || T % kGroup != 0 || F % kGroup != 0 || ld < F || T / kGroup > kMaxGridY)
+        return FP8LIN_ERR_SHAPE;
+    int64_t F2, bdh, bq, bs, bsT, span;
+    if (!mul_ok(F, 2, &F2) || !bytes_of(T, F, 2, &bdh) || !bytes_of(T, F2, 1, &bq) ||
+        !bytes_of(T, F2 / kGroup, 4, &bs) || !bytes_of(F2, T / kGroup, 4, &bsT))
+        return FP8LIN_ERR_SHAPE;
+    if (bq == 0)
+        return FP8LIN_OK;
+    if (!mul_ok(T - 1, ld, &span) || span > INT64_MAX / 2 - F)
+        return FP8LIN_ERR_SHAPE;
+    const int64_t bin = (span + F) * 2;
+    if (ld % 8 != 0)
+        return FP8LIN_ERR_ALIGN;
+    const Buf in[] = {{gate, bin}, {up, bin}, {dh, bdh}};
+    const Buf out[] = {{dguq, bq}, {sdgu, bs}, {dguTq, bq}, {sdguT, bsT}};
+    fp8lin_status s = check_buffers(in, 3, out, 4);
+    if (s != FP8LIN_OK)
+        return s;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_swiglu_bwd_quant(gate, up, ld, dh, T, F, dguq, sdgu, dguTq, sdguT, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_mlp_fwd(const void* x, const void* gamma, float eps, const uint8_t* wgu, const float* sgu,
                           const uint8_t* wdown, const float* sdown, int64_t T, int64_t K, int64_t F, uint8_t* xq,
                           float* sx, float* rstd, void* gu, uint8_t* hq, float* sh, void* y, void* stream)

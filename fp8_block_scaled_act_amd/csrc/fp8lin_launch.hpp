@@ -25,6 +25,8 @@ void launch_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M
                          float* s, hipStream_t st);
 void launch_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void* dh, int64_t M, int64_t F,
                        void* dgu, hipStream_t st);
+void launch_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const void* dh, int64_t T, int64_t F,
+                             uint8_t* q, float* s, uint8_t* qT, float* sT, hipStream_t st);
 
 void launch_fill_zero_bf16(void* c, int64_t n, hipStream_t st);
 void launch_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,

@@ -19,6 +19,7 @@
 //             cannot decide the rounding).
 #include "fp8lin_device.hpp"
 #include "fp8lin_launch.hpp"
+#include "quant_tile.hpp"
 
 namespace fp8lin {
 
@@ -364,6 +365,50 @@ __device__ __forceinline__ void swiglu_bwd_f32(float g, float u, float dh, float
     redo = ag >= 64.0f || !(bg < 65536.0f) || needs_f64(vu, bu) || needs_f64(vg, bg);
 }
 
+// The 8 (d_gate, d_up) pairs of 16-byte chunks of g, u and dh.
+__device__ __forceinline__ void swiglu_bwd8(uint4 gv, uint4 uv, uint4 dv, uint4& og4, uint4& ou4)
+{
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+    uint32_t og[4], ou[4];
+    uint32_t need = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float vg0, vu0, vg1, vu1;
+        bool r0, r1;
+        swiglu_bwd_f32(bf16_lo(gw[j]), bf16_lo(uw[j]), bf16_lo(dw[j]), vg0, vu0, r0);
+        swiglu_bwd_f32(bf16_hi(gw[j]), bf16_hi(uw[j]), bf16_hi(dw[j]), vg1, vu1, r1);
+        og[j] = pack_bf16x2(vg0, vg1);
+        ou[j] = pack_bf16x2(vu0, vu1);
+        need |= (r0 ? 1u << (2 * j) : 0u) | (r1 ? 2u << (2 * j) : 0u);
+    }
+    while (need != 0) {                                     // divergent: flagged elements only
+        const int k = __builtin_ctz(need);
+        need &= need - 1;
+        uint32_t gs = 0, us = 0, ds = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((k >> 1) == j) {
+                gs = gw[j];
+                us = uw[j];
+                ds = dw[j];
+            }
+        const bool hi = k & 1;
+        uint32_t bg, bu;
+        swiglu_bwd_f64(hi ? bf16_hi(gs) : bf16_lo(gs), hi ? bf16_hi(us) : bf16_lo(us),
+                       hi ? bf16_hi(ds) : bf16_lo(ds), bg, bu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((k >> 1) == j) {
+                og[j] = hi ? ((og[j] & 0xFFFFu) | (bg << 16)) : ((og[j] & 0xFFFF0000u) | bg);
+                ou[j] = hi ? ((ou[j] & 0xFFFFu) | (bu << 16)) : ((ou[j] & 0xFFFF0000u) | bu);
+            }
+    }
+    og4 = make_uint4(og[0], og[1], og[2], og[3]);
+    ou4 = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+}
+
 // A thread owns 8 consecutive columns of one row (16-byte loads of g, u, dh;
 // 16-byte stores of d_gate into dgu[:, :F] and d_up into dgu[:, F:]).
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restrict__ gate,
@@ -374,49 +419,70 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
     const int64_t cpr = F >> 3;                             // 8-column chunks per row
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += (int64_t)gridDim.x * 256) {
         const int64_t m = i / cpr, c = (i - m * cpr) * 8;
-        const uint4 gv = load_nt(gate + m * ld + c);
-        const uint4 uv = load_nt(up + m * ld + c);
-        const uint4 dv = load_nt(dh + m * F + c);
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-        const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
-        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
-        uint32_t og[4], ou[4];
-        uint32_t need = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float vg0, vu0, vg1, vu1;
-            bool r0, r1;
-            swiglu_bwd_f32(bf16_lo(gw[j]), bf16_lo(uw[j]), bf16_lo(dw[j]), vg0, vu0, r0);
-            swiglu_bwd_f32(bf16_hi(gw[j]), bf16_hi(uw[j]), bf16_hi(dw[j]), vg1, vu1, r1);
-            og[j] = pack_bf16x2(vg0, vg1);
-            ou[j] = pack_bf16x2(vu0, vu1);
-            need |= (r0 ? 1u << (2 * j) : 0u) | (r1 ? 2u << (2 * j) : 0u);
-        }
-        while (need != 0) {                                 // divergent: flagged elements only
-            const int k = __builtin_ctz(need);
-            need &= need - 1;
-            uint32_t gs = 0, us = 0, ds = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if ((k >> 1) == j) {
-                    gs = gw[j];
-                    us = uw[j];
-                    ds = dw[j];
-                }
-            const bool hi = k & 1;
-            uint32_t bg, bu;
-            swiglu_bwd_f64(hi ? bf16_hi(gs) : bf16_lo(gs), hi ? bf16_hi(us) : bf16_lo(us),
-                           hi ? bf16_hi(ds) : bf16_lo(ds), bg, bu);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if ((k >> 1) == j) {
-                    og[j] = hi ? ((og[j] & 0xFFFFu) | (bg << 16)) : ((og[j] & 0xFFFF0000u) | bg);
-                    ou[j] = hi ? ((ou[j] & 0xFFFFu) | (bu << 16)) : ((ou[j] & 0xFFFF0000u) | bu);
-                }
-        }
+        uint4 og, ou;
+        swiglu_bwd8(load_nt(gate + m * ld + c), load_nt(up + m * ld + c), load_nt(dh + m * F + c), og, ou);
         uint16_t* row = dgu + m * 2 * F + c;
-        *reinterpret_cast<uint4*>(row) = make_uint4(og[0], og[1], og[2], og[3]);
-        *reinterpret_cast<uint4*>(row + F) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+        *reinterpret_cast<uint4*>(row) = og;
+        *reinterpret_cast<uint4*>(row + F) = ou;
+    }
+}
+
+// =========================== SwiGLU backward fused with its FP8 quantization
+//
+// The gradient of the fused gate/up projection's output, dgu = [d_gate | d_up]
+// [T, 2F], is consumed only as FP8: 1x128 row groups by the gate/up DGrad and
+// 128-along-token groups (transposed) by its WGrad.  One workgroup per
+// 128 (tokens) x 128 (columns of g, u, dh) tile computes both gradients of
+// the tile in registers (swiglu_bwd8 on 8 rows x 8 columns per
+// thread), writes their row quantization directly (gate columns f0.., up
+// columns F + f0..), then parks each half in LDS in turn for the transposing
+// quantizer's column phase.  dgu itself is never stored; the codes and scales
+// are bit-identical to fp8_quant_transpose (dual) of fp8_swiglu_bwd's output.
+__global__ __launch_bounds__(256) void swiglu_bwd_quant_kernel(const uint16_t* __restrict__ gate,
+                                                               const uint16_t* __restrict__ up, int64_t ld,
+                                                               const uint16_t* __restrict__ dh, int64_t T,
+                                                               int64_t F, uint8_t* __restrict__ q,
+                                                               float* __restrict__ s, uint8_t* __restrict__ qT,
+                                                               float* __restrict__ sT)
+{
+    __shared__ uint4 tile[128 * 16];              // [row][16 chunks of 8 bf16] = 32 KB
+    __shared__ uint32_t red[4 * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t ctile[128 * 128];
+    const int tid = threadIdx.x;
+    const int sub = tid & 15, r0 = tid >> 4;
+    const int64_t t0 = (int64_t)blockIdx.y * kGroup, f0 = (int64_t)blockIdx.x * kGroup;
+    const int64_t F2 = 2 * F, G2 = F2 / kGroup;
+    uint4 vg[8], vu[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = t0 + r0 + 16 * i, col = f0 + sub * 8;
+        swiglu_bwd8(load_nt(gate + row * ld + col), load_nt(up + row * ld + col), load_nt(dh + row * F + col),
+                    vg[i], vu[i]);
+    }
+    // 1x128 row groups of both halves
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = t0 + r0 + 16 * i;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 v = h ? vu[i] : vg[i];
+            const int64_t col = (h ? F : 0) + f0;
+            const GroupScale gs = group_scale(max_over_16_lanes(absmax_bits_8xbf16(v)));
+            *reinterpret_cast<uint2*>(q + row * F2 + col + sub * 8) = quantize8(v, gs);
+            if (sub == 0)
+                s[row * G2 + col / kGroup] = gs.s;
+        }
+    }
+    // 128-along-token groups, transposed: the gate half, then the up half
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h)
+            __syncthreads();                          // the gate half's tile and code tile are drained
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            tile[(r0 + 16 * i) * 16 + sub] = h ? vu[i] : vg[i];
+        __syncthreads();
+        transpose_quant_tile<false>(tile, red, ctile, qT, sT, (h ? F : 0) + f0, t0, T, F2);
     }
 }
 
@@ -478,6 +544,18 @@ void launch_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void*
     swiglu_bwd_kernel<<<(unsigned)(blocks < 1 ? 1 : blocks), 256, 0, st>>>(
         static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up), ld, static_cast<const uint16_t*>(dh),
         F, nchunks, static_cast<uint16_t*>(dgu));
+}
+
+}  // namespace fp8lin
+
+namespace fp8lin {
+
+void launch_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const void* dh, int64_t T, int64_t F,
+                             uint8_t* q, float* s, uint8_t* qT, float* sT, hipStream_t st)
+{
+    const dim3 grid((unsigned)(F / kGroup), (unsigned)(T / kGroup));
+    swiglu_bwd_quant_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up),
+                                                  ld, static_cast<const uint16_t*>(dh), T, F, q, s, qT, sT);
 }
 
 }  // namespace fp8lin

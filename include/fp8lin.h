@@ -290,6 +290,24 @@ fp8lin_status fp8_swiglu_bwd(const void* gate, const void* up, int64_t ld, const
                              int64_t M, int64_t F, void* dgu, void* stream);
 
 /*
+ * SwiGLU backward fused with the FP8 quantization of its result for the
+ * gate/up projection's DGrad and WGrad (Jet-RL summary, "Quantization
+ * scheme": FP8 backward GEMMs with 1x128 and 128x1 groups; "Implementation":
+ * fused activation kernels).  The BF16 gradient dgu = [d_gate | d_up] of
+ * fp8_swiglu_bwd is computed tile by tile in registers and never stored;
+ * the outputs are bit-identical to fp8_quant_transpose(dgu, dual):
+ *   gate, up : BF16, rows of F elements at row stride ld; dh : BF16 [T,F]
+ *   dguq  : uint8 [T,2F],  sdgu  : float [T][2F/128]   (1x128 row groups)
+ *   dguTq : uint8 [2F,T],  sdguT : float [2F][T/128]   (128-along-T groups, transposed)
+ * T % 128 == 0, F % 128 == 0, ld >= F, T / 128 <= 65535, else
+ * FP8LIN_ERR_SHAPE; ld % 8 != 0: FP8LIN_ERR_ALIGN.  T == 0 or F == 0 is an
+ * OK no-op.
+ */
+fp8lin_status fp8_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const void* dh,
+                                   int64_t T, int64_t F, uint8_t* dguq, float* sdgu,
+                                   uint8_t* dguTq, float* sdguT, void* stream);
+
+/*
  * Forward pass of an FP8 MLP block (RMSNorm, gate/up projection, SwiGLU,
  * down projection) in one call: the unified FP8 flow of the Jet-RL summary
  * ("Core architecture": rollout and training forward share it; "Quantization

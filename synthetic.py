@@ -129,8 +129,8 @@ WORKLOADS = {
     "mlp_train": Workload("mlp_train", "mlp_train", 8192, 14336, 4096, n_outliers(4096),
                           "8B-shaped FP8 MLP block training step on 8192 tokens: forward (RMSNorm->FP8, gate/up "
                           "GEMM, SwiGLU->FP8, down GEMM) and backward through the three linear layers (dual "
-                          "transpose-quant of dY and dGU, FP8-source requant of H and X, SwiGLU backward, two "
-                          "DGrad and two WGrad GEMMs)"),
+                          "transpose-quant of dY, FP8-source requant of H and X, SwiGLU backward fused with the "
+                          "dual quantization of its result, two DGrad and two WGrad GEMMs)"),
     "producers": Workload("producers", "producers", 8192, 14336, 4096, n_outliers(4096),
                           "8B-shaped producers fused with 1x128 quantization: RMSNorm of X[8192,4096], "
                           "SwiGLU of the gate/up halves of one [8192,2x14336] projection output"),

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
               "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
               "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
               "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed_splitk",
-              "fp8_gemm_fwd_packed_splitk_workspace", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_gemm_fwd_packed_splitk_workspace", "fp8_swiglu_bwd_quant", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -253,6 +253,18 @@ def test_swiglu_bwd_validation(L):
     assert L.fp8_swiglu_bwd(A, B, 256, C, 4, 256, C + 64, s0) == ALIAS     # dgu over dh
     assert L.fp8_swiglu_bwd(A, A + 256, 512, C, 4, 256, D, s0) == DEVICE   # halves of one tensor
     assert L.fp8_swiglu_bwd(None, None, 256, None, 0, 256, None, s0) == OK
+
+
+@fake_ptrs
+def test_swiglu_bwd_quant_validation(L):
+    # gate, up, ld, dh, T, F, dguq, sdgu, dguTq, sdguT
+    assert L.fp8_swiglu_bwd_quant(A, B, 256, C, 100, 256, D, E, F, A + 2 ** 26, s0) == SHAPE     # T % 128
+    assert L.fp8_swiglu_bwd_quant(A, B, 256, C, 128, 200, D, E, F, A + 2 ** 26, s0) == SHAPE     # F % 128
+    assert L.fp8_swiglu_bwd_quant(A, B, 260, C, 128, 256, D, E, F, A + 2 ** 26, s0) == ALIGN
+    assert L.fp8_swiglu_bwd_quant(A, B, 256, None, 128, 256, D, E, F, A + 2 ** 26, s0) == NULL
+    assert L.fp8_swiglu_bwd_quant(A, B, 256, C, 128, 256, D, E, D + 64, A + 2 ** 26, s0) == ALIAS
+    assert L.fp8_swiglu_bwd_quant(None, None, 256, None, 0, 256, None, None, None, None, s0) == OK
+    assert L.fp8_swiglu_bwd_quant(A, B, 256, C, 128, 256, D, E, F, A + 2 ** 26, s0) == DEVICE
 
 
 @fake_ptrs
