@@ -192,10 +192,12 @@ def build_step(name, torch, fl, synthetic):
         x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
         gamma = bf16(synthetic.norm_weights(K, seed=0))
         dy = bf16(synthetic.grad_out(T, K, seed=0))
-        wgu, sgu = fl.fp8_quant_weight(bf16(synthetic.weights(2 * F, K, seed=0)))
-        wd, sd = fl.fp8_quant_weight(bf16(synthetic.weights(K, F, seed=1)))
-        wguT, sguT = fl.fp8_weight_transpose(wgu, sgu)     # made with the weight quantization
-        wdT, sdT = fl.fp8_weight_transpose(wd, sd)
+        wgu_b = bf16(synthetic.weights(2 * F, K, seed=0))     # BF16 master weights
+        wd_b = bf16(synthetic.weights(K, F, seed=1))
+        wgu, sgu = empty((2 * F, K), u8), empty((2 * F // G, K // G), f32)
+        wd, sd = empty((K, F), u8), empty((K // G, F // G), f32)
+        wguT, sguT = empty((K, 2 * F), u8), empty((K // G, 2 * F // G), f32)
+        wdT, sdT = empty((F, K), u8), empty((F // G, K // G), f32)
         torch.cuda.synchronize()
         xq, sx, rstd = empty((T, K), u8), empty((T, K // G), f32), empty((T,), f32)
         gu, hq, sh, y = empty((T, 2 * F), bf), empty((T, F), u8), empty((T, F // G), f32), empty((T, K), bf)
@@ -208,6 +210,16 @@ def build_step(name, torch, fl, synthetic):
         dwgu, dxn = empty((2 * F, K), bf), empty((T, K), bf)
         dual = lambda r, c: r * c * 2 + 2 * r * c + (c * (r // G) + r * (c // G)) * 4
         requant = lambda r, c: 2 * r * c + (r * (c // G) + c * (r // G)) * 4
+        # per optimizer step: the weights re-quantized from the BF16 masters, with
+        # the transposed copies DGrad reads
+        st.add("quant_weight_gate_up", lambda i: fl.fp8_quant_weight(wgu_b, out=(wgu, sgu)), "hbm",
+               weight_quant_bytes(2 * F, K))
+        st.add("quant_weight_down", lambda i: fl.fp8_quant_weight(wd_b, out=(wd, sd)), "hbm",
+               weight_quant_bytes(K, F))
+        st.add("weight_transpose_gate_up", lambda i: fl.fp8_weight_transpose(wgu, sgu, out=(wguT, sguT)), "hbm",
+               2 * 2 * F * K + 2 * (2 * F // G) * (K // G) * 4)
+        st.add("weight_transpose_down", lambda i: fl.fp8_weight_transpose(wd, sd, out=(wdT, sdT)), "hbm",
+               2 * K * F + 2 * (K // G) * (F // G) * 4)
         st.add("rmsnorm_quant", lambda i: fl.fp8_rmsnorm_quant(x, gamma, 1e-6, out=(xq, sx, rstd)), "hbm",
                act_quant_bytes(T, K) + 4 * T + 2 * K)
         st.add("gemm_gate_up", lambda i: fl.fp8_gemm_fwd(xq, sx, wgu, sgu, out=gu), "mfma", 4 * T * F * K)
@@ -233,8 +245,8 @@ def build_step(name, torch, fl, synthetic):
         st.gemm_flop = 18 * T * K * F
         st.config = {"workload": wl.doc, "T": T, "K": K, "F": F, "eps": 1e-6, "outlier_columns": wl.n_out,
                      "same_kernels_as": "fp8_mlp_fwd + fp8_mlp_bwd",
-                     "dgrad_weights": "transposed FP8 copies (fp8_weight_transpose), made with the weight "
-                                      "quantization outside the step"}
+                     "weights": "re-quantized from BF16 masters inside the step (fp8_quant_weight), with "
+                                "the transposed FP8 copies DGrad reads (fp8_weight_transpose)"}
     elif wl.kind == "producers":
         T, F, K = wl.M, wl.N, wl.K
         x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
@@ -435,6 +447,10 @@ KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes f
     "gemm_wgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_wgrad_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "quant_weight_gate_up": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "quant_weight_down": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "weight_transpose_gate_up": ("quant_kernels.hip", "fp8lin_device.hpp"),
+    "weight_transpose_down": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "gemm_dgrad_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_wgrad_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "gemm_dgrad_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
@@ -457,7 +473,11 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "gemm_fwd": "gemm_",
     "gemm_dgrad": "Mode)0",     # the backward step runs DGrad as the NT GEMM on W^T
     "gemm_wgrad": "Mode)2",
-    "gemm_wgrad_down": None,    # GEMMs of one kernel at several shapes: counters cannot tell them apart
+    "gemm_wgrad_down": None,    # kernels run at several shapes in one step: counters cannot tell them apart
+    "quant_weight_gate_up": None,
+    "quant_weight_down": None,
+    "weight_transpose_gate_up": None,
+    "weight_transpose_down": None,
     "gemm_dgrad_down": None,
     "gemm_wgrad_gate_up": None,
     "gemm_dgrad_gate_up": None,

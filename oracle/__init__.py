@@ -67,11 +67,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_rmsnorm_bf16.argtypes = [u16p, u16p, i64, i64, ctypes.c_float, u16p, f32p]
         L.oracle_swiglu_bf16.argtypes = [u16p, u16p, i64, i64, i64, u16p, u8p]
         L.oracle_swiglu_bwd_bf16.argtypes = [u16p, u16p, u16p, i64, i64, i64, u16p, u8p]
+        L.oracle_rmsnorm_bwd.argtypes = [u16p, u16p, f32p, u16p, i64, i64, u16p, f32p]
         L.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_quant_act", "oracle_quant_weight", "oracle_quant_transpose_bf16",
                   "oracle_quant_transpose_fp8", "oracle_dequant_rowgroup",
                   "oracle_dequant_block", "oracle_gemm", "oracle_rmsnorm_bf16",
-                  "oracle_swiglu_bf16", "oracle_swiglu_bwd_bf16"):
+                  "oracle_swiglu_bf16", "oracle_swiglu_bwd_bf16", "oracle_rmsnorm_bwd"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -195,6 +196,20 @@ def swiglu_bf16(gate_bf16: np.ndarray, up_bf16: np.ndarray):
     lib().oracle_swiglu_bf16(_ptr(g, ctypes.c_uint16), _ptr(u, ctypes.c_uint16), F, M, F,
                              _ptr(h, ctypes.c_uint16), _ptr(t, ctypes.c_uint8))
     return h, t.astype(bool)
+
+
+def rmsnorm_bwd(x_bf16: np.ndarray, gamma_bf16: np.ndarray, rstd: np.ndarray, dy_bf16: np.ndarray):
+    """RMSNorm backward: x, dy bf16 [M,K], gamma bf16 [K], rstd f32 [M] (the
+    forward's) -> (dx bf16 bits [M,K], dgamma f32 [K]), fp64 in a fixed order."""
+    x, g, d = _bits16(x_bf16), _bits16(gamma_bf16), _bits16(dy_bf16)
+    r = np.ascontiguousarray(rstd, dtype=np.float32)
+    M, K = x.shape
+    assert K % GROUP == 0 and g.shape == (K,) and d.shape == (M, K) and r.shape == (M,)
+    dx = np.empty((M, K), np.uint16)
+    dg = np.empty((K,), np.float32)
+    lib().oracle_rmsnorm_bwd(_ptr(x, ctypes.c_uint16), _ptr(g, ctypes.c_uint16), _ptr(r, ctypes.c_float),
+                             _ptr(d, ctypes.c_uint16), M, K, _ptr(dx, ctypes.c_uint16), _ptr(dg, ctypes.c_float))
+    return dx, dg
 
 
 def swiglu_bwd_bf16(gate_bf16: np.ndarray, up_bf16: np.ndarray, dh_bf16: np.ndarray):

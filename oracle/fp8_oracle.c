@@ -361,6 +361,66 @@ void oracle_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t M, in
     }
 }
 
+/*
+ * Backward of the RMSNorm above, y = x * r * gamma, with r the rstd the
+ * forward saved (the rounding of y is passed straight through).  From
+ * dr/dx_i = -r^3 x_i / K, the textbook gradients are
+ *   dx_j     = r g_j - x_j r^3 c / K,   g_j = gamma_j dy_j,   c = sum_i g_i x_i
+ *   dgamma_k = sum_t dy[t,k] x[t,k] r_t
+ * evaluated in fp64 in a fixed order:
+ *   g_i = gamma_i * dy_i and p_i = g_i * x_i (both exact);
+ *   c = sum of p over the row: each 128-group a balanced binary tree, the
+ *       group sums added in ascending order (the forward's order for ss);
+ *   k = ((r * r) * r) * (c / K);  dx_j = bf16(r * g_j - x_j * k), one rounding;
+ *   dgamma_k = fp32 of the sum over t of (dy * x) * r_t, the rows of each block
+ *       of 128 rows added in ascending order from 0, the block sums added in
+ *       ascending order from 0 (a last block may be shorter).
+ * x, dy: BF16 [M,K]; gamma: BF16 [K]; rstd: fp32 [M]; dx: BF16 [M,K];
+ * dgamma: fp32 [K] (may be NULL).
+ */
+void oracle_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, const float* rstd, const uint16_t* dy,
+                        int64_t M, int64_t K, uint16_t* dx, float* dgamma)
+{
+    int64_t G = K / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* xr = x + m * K;
+        const uint16_t* dr = dy + m * K;
+        double p[GROUP];
+        double c = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            for (int i = 0; i < GROUP; ++i) {
+                int64_t k = g * GROUP + i;
+                double gi = (double)oracle_bf16_to_f32(gamma[k]) * (double)oracle_bf16_to_f32(dr[k]);
+                p[i] = gi * (double)oracle_bf16_to_f32(xr[k]);
+            }
+            c += tree_sum(p, GROUP);
+        }
+        double r = (double)rstd[m];
+        double kk = ((r * r) * r) * (c / (double)K);
+        for (int64_t k = 0; k < K; ++k) {
+            double gi = (double)oracle_bf16_to_f32(gamma[k]) * (double)oracle_bf16_to_f32(dr[k]);
+            double v = r * gi - (double)oracle_bf16_to_f32(xr[k]) * kk;
+            dx[m * K + k] = oracle_f64_to_bf16(v);
+        }
+    }
+    if (!dgamma)
+        return;
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k) {
+        double total = 0.0;
+        for (int64_t b0 = 0; b0 < M; b0 += GROUP) {
+            double block = 0.0;
+            for (int64_t t = b0; t < M && t < b0 + GROUP; ++t) {
+                double prod = (double)oracle_bf16_to_f32(dy[t * K + k]) * (double)oracle_bf16_to_f32(x[t * K + k]);
+                block += prod * (double)rstd[t];
+            }
+            total += block;
+        }
+        dgamma[k] = (float)total;
+    }
+}
+
 /* Flag for a fp64 value whose BF16 rounding is within 2^-44 (relative) of a
  * midpoint between two BF16 neighbours (either neighbour is then correct). */
 static uint8_t bf16_near_tie(double v)

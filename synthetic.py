@@ -127,7 +127,8 @@ WORKLOADS = {
                            "8B-shaped FP8 MLP block rollout decode step on 64 tokens: RMSNorm->FP8, gate/up GEMM "
                            "[28672,4096], SwiGLU->FP8, down GEMM [4096,14336], weights pre-quantized and packed"),
     "mlp_train": Workload("mlp_train", "mlp_train", 8192, 14336, 4096, n_outliers(4096),
-                          "8B-shaped FP8 MLP block training step on 8192 tokens: forward (RMSNorm->FP8, gate/up "
+                          "8B-shaped FP8 MLP block training step on 8192 tokens: weight re-quantization from BF16 "
+                          "masters (with transposed copies), forward (RMSNorm->FP8, gate/up "
                           "GEMM, SwiGLU->FP8, down GEMM) and backward through the three linear layers (dual "
                           "transpose-quant of dY, FP8-source requant of H and X, SwiGLU backward fused with the "
                           "dual quantization of its result, two DGrad and two WGrad GEMMs)"),

@@ -329,3 +329,85 @@ def test_swiglu_bwd_special_values():
     assert np.all(dg[:32] == -0.75) and np.all(du[:32] == 0.0)
     assert np.all(dg[32:64] == -1.5) and np.all(du[32:64] == -64.0)
     assert np.all(dg[64:96] == 0.0) and np.all(du[64:96] == 0.0)
+
+
+# -------------------------------------------------------- RMSNorm backward
+
+def test_rmsnorm_bwd_matches_exact_rationals():
+    """dx and dgamma against exact rational evaluation of the textbook
+    gradients with the forward's rstd: dx bit-exact wherever the fp64
+    evaluation error cannot reach a bf16 midpoint, dgamma equal to the fp32
+    rounding of the exact sum (pins the r^3 term, its sign, the 1/K, gamma's
+    place and the accumulation over tokens)."""
+    M, K = 6, 256
+    x = synthetic.activations(M, K, seed=31, n_out=2)
+    gamma = synthetic.norm_weights(K, seed=31)
+    dy = synthetic.grad_out(M, K, seed=31, sigma=1.0)
+    _, rstd = oracle.rmsnorm_bf16(x, gamma, 1e-6)
+    dx, dg = oracle.rmsnorm_bwd(x, gamma, rstd, dy)
+    xf, gf, df = f32(x), f32(gamma), f32(dy)
+    checked = 0
+    for m in range(M):
+        r = Fraction(float(rstd[m]))
+        gi = [Fraction(float(gf[k])) * Fraction(float(df[m, k])) for k in range(K)]
+        xs = [Fraction(float(xf[m, k])) for k in range(K)]
+        c = sum(g * xv for g, xv in zip(gi, xs))
+        kk = r * r * r * c / K
+        for k in range(K):
+            a, b = r * gi[k], xs[k] * kk
+            exact = a - b
+            want = round_fraction(exact, 8, -126)
+            if exact != 0 and abs(exact - (want if want != 0 else exact)) >= 0:
+                margin = midpoint_distance(exact, 8, -126) * abs(exact) if exact != 0 else Fraction(1)
+                if margin <= (abs(a) + abs(b)) * Fraction(1, 2 ** 48):
+                    continue
+            assert Fraction(float(f32(dx[m, k]))) == want, (m, k)
+            checked += 1
+    assert checked > 0.99 * M * K
+    for k in range(0, K, 7):
+        total = sum(Fraction(float(df[t, k])) * Fraction(float(xf[t, k])) * Fraction(float(rstd[t]))
+                    for t in range(M))
+        assert np.float32(dg[k]) == np.float32(float(total)), k
+
+
+def test_rmsnorm_bwd_library_autograd():
+    """Against torch autograd of x * rsqrt(mean(x^2) + eps) * gamma in float64
+    (its own r, not the saved fp32 rstd): dx within one bf16 rounding plus
+    2^-20 of the two terms' magnitude, dgamma within 2^-20 of the sum of the
+    terms' magnitudes (the saved rstd is the fp32 rounding of torch's r); over
+    more than one block of 128 tokens."""
+    M, K, eps = 300, 512, 1e-6
+    x = synthetic.activations(M, K, seed=32, n_out=2)
+    gamma = synthetic.norm_weights(K, seed=32)
+    dy = synthetic.grad_out(M, K, seed=32, sigma=1.0)
+    _, rstd = oracle.rmsnorm_bf16(x, gamma, eps)
+    dx, dg = oracle.rmsnorm_bwd(x, gamma, rstd, dy)
+    xt = torch.from_numpy(f32(x).astype(np.float64)).requires_grad_(True)
+    gt = torch.from_numpy(f32(gamma).astype(np.float64)).requires_grad_(True)
+    y = xt * torch.rsqrt((xt * xt).mean(dim=1, keepdim=True) + eps) * gt
+    y.backward(torch.from_numpy(f32(dy).astype(np.float64)))
+    want = xt.grad.numpy()
+    r = rstd.astype(np.float64)[:, None]
+    g = f32(gamma).astype(np.float64)[None, :] * f32(dy).astype(np.float64)
+    scale = np.abs(r * g) + np.abs(f32(x) * r ** 3 * (g * f32(x)).sum(axis=1, keepdims=True) / K)
+    err = np.abs(f32(dx).astype(np.float64) - want)
+    assert np.all(err <= 2.0 ** -8 * np.abs(want) + 2.0 ** -20 * scale)
+    mag = (np.abs(f32(dy).astype(np.float64) * f32(x)) * rstd.astype(np.float64)[:, None]).sum(axis=0)
+    assert np.all(np.abs(dg.astype(np.float64) - gt.grad.numpy()) <= 2.0 ** -20 * mag)
+
+
+def test_rmsnorm_bwd_invariants():
+    """y is invariant to scaling x (eps = 0), so dx is orthogonal to x up to
+    rounding; dy = 0 gives zero gradients."""
+    M, K = 8, 1024
+    x = synthetic.activations(M, K, seed=33, n_out=2)
+    gamma = synthetic.norm_weights(K, seed=33)
+    dy = synthetic.grad_out(M, K, seed=33, sigma=1.0)
+    _, rstd = oracle.rmsnorm_bf16(x, gamma, 0.0)
+    dx, _ = oracle.rmsnorm_bwd(x, gamma, rstd, dy)
+    xd = f32(x).astype(np.float64)
+    dxd = f32(dx).astype(np.float64)
+    dot = np.abs((xd * dxd).sum(axis=1))
+    assert np.all(dot <= 2.0 ** -6 * (np.abs(xd * dxd)).sum(axis=1))
+    dx0, dg0 = oracle.rmsnorm_bwd(x, gamma, rstd, np.zeros_like(dy))
+    assert np.all((dx0 & 0x7FFF) == 0) and np.all(dg0 == 0)
