@@ -241,10 +241,14 @@ def build_step(name, torch, fl, synthetic):
                4 * T * F * K)
         st.add("gemm_dgrad_gate_up", lambda i: fl.fp8_gemm_dgrad_t(dguq, sdgu, wguT, sguT, out=dxn), "mfma",
                4 * T * F * K)
+        dxb, dgam = empty((T, K), bf), empty((K,), f32)
+        wsn = torch.empty((fl.fp8_rmsnorm_bwd_workspace(T, K) // 8,), dtype=torch.float64, device=dev)
+        st.add("rmsnorm_bwd", lambda i: fl.fp8_rmsnorm_bwd(x, gamma, rstd, dxn, workspace=wsn, out=(dxb, dgam)),
+               "hbm", 3 * T * K * 2 + 4 * T + 2 * K + 4 * K)
         st.dominant = None
         st.gemm_flop = 18 * T * K * F
         st.config = {"workload": wl.doc, "T": T, "K": K, "F": F, "eps": 1e-6, "outlier_columns": wl.n_out,
-                     "same_kernels_as": "fp8_mlp_fwd + fp8_mlp_bwd",
+                     "same_kernels_as": "fp8_mlp_fwd + fp8_mlp_bwd (with the RMSNorm backward)",
                      "weights": "re-quantized from BF16 masters inside the step (fp8_quant_weight), with "
                                 "the transposed FP8 copies DGrad reads (fp8_weight_transpose)"}
     elif wl.kind == "producers":
@@ -457,6 +461,7 @@ KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes f
     "quant_transpose_fp8_H": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "quant_transpose_dual_dGU": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_bwd": ("producer_kernels.hip", "fp8lin_device.hpp"),
+    "rmsnorm_bwd": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_bwd_quant": ("producer_kernels.hip", "quant_tile.hpp", "fp8lin_device.hpp"),
     "gemm_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "rmsnorm_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
@@ -484,6 +489,7 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "quant_transpose_fp8_H": None,
     "quant_transpose_dual_dGU": None,
     "swiglu_bwd": "swiglu_bwd_kernel",
+    "rmsnorm_bwd": None,        # three kernels (dx, dgamma block sums, dgamma total)
     "swiglu_bwd_quant": "swiglu_bwd_quant_kernel",
     "gemm_gate_up": None,       # same kernel as gemm_down: counters cannot tell them apart
     "gemm_down": None,

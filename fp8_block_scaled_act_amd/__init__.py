@@ -23,7 +23,7 @@ __all__ = [
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
     "fp8_gemm_fwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed",
     "fp8_gemm_fwd_packed_splitk", "fp8_gemm_fwd_packed_splitk_workspace", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
-    "fp8_rmsnorm_quant", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_swiglu_bwd_quant", "fp8_mlp_fwd", "fp8_mlp_bwd",
+    "fp8_rmsnorm_quant", "fp8_rmsnorm_bwd", "fp8_rmsnorm_bwd_workspace", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_swiglu_bwd_quant", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -63,6 +63,9 @@ _SYMBOLS = {
     "fp8_gemm_wgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_rmsnorm_quant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "fp8_rmsnorm_bwd_workspace": ([ctypes.c_int64] * 2, ctypes.c_int64),
+    "fp8_rmsnorm_bwd": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 3 +
+                        [ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
     "fp8_swiglu_quant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "fp8_swiglu_bwd": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
@@ -347,6 +350,40 @@ def fp8_rmsnorm_quant(x, gamma, eps: float = 1e-6, out=None, rstd: bool = True, 
     return q, s, r
 
 
+def fp8_rmsnorm_bwd_workspace(M: int, K: int) -> int:
+    n = lib().fp8_rmsnorm_bwd_workspace(M, K)
+    if n < 0:
+        raise Fp8LinError(2, "fp8_rmsnorm_bwd_workspace")
+    return n
+
+
+def fp8_rmsnorm_bwd(x, gamma, rstd, dy, dgamma: bool = True, workspace=None, out=None, stream=None):
+    """Backward of fp8_rmsnorm_quant's RMSNorm: x, dy bf16 [M,K], gamma bf16 [K],
+    rstd f32 [M] -> (dx bf16 [M,K], dgamma f32 [K] or None).  workspace: a
+    float64 CUDA tensor of fp8_rmsnorm_bwd_workspace bytes (allocated here when
+    None)."""
+    M, K = x.shape
+    _expect(x, "x", torch.bfloat16, (M, K))
+    _expect(dy, "dy", torch.bfloat16, (M, K))
+    _expect(gamma, "gamma", torch.bfloat16, (K,))
+    _expect(rstd, "rstd", torch.float32, (M,))
+    if out is None:
+        dx = _empty((M, K), torch.bfloat16, x)
+        dg = _empty((K,), torch.float32, x) if dgamma else None
+    else:
+        dx, dg = out
+    _expect(dx, "dx", torch.bfloat16, (M, K))
+    if dg is not None:
+        _expect(dg, "dgamma", torch.float32, (K,))
+    need = fp8_rmsnorm_bwd_workspace(M, K) if dg is not None else 0
+    if workspace is None and need:
+        workspace = _empty((need // 8,), torch.float64, x)
+    nbytes = workspace.numel() * 8 if workspace is not None else 0
+    _check(lib().fp8_rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(rstd), _ptr(dy), M, K, _ptr(dx), _ptr(dg),
+                                 _ptr(workspace), nbytes, _stream(stream)), "fp8_rmsnorm_bwd")
+    return dx, dg
+
+
 def fp8_swiglu_quant(gate, up, out=None, stream=None):
     """silu(gate) * up of bf16 [M,F] operands, quantized 1x128 without storing
     the BF16 product: returns (hq u8 [M,F], sh f32 [M,F/128]).  gate and up may
@@ -466,7 +503,7 @@ def fp8_mlp_fwd(x, gamma, wgu, sgu, wdown, sdown, eps: float = 1e-6, out=None, r
     return out
 
 
-def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, stream=None):
+def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, x=None, gamma=None, stream=None):
     """Backward pass of the FP8 MLP block through its three linear layers, as a
     fixed sequence of C-ABI calls on one stream (every step runs in the
     library's kernels; this function only allocates the intermediates):
@@ -480,11 +517,14 @@ def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, stream=None):
       fp8_quant_transpose(xq, sx)             -> X^T q        (saved FP8 block input)
       fp8_gemm_wgrad(dGU^T q, X^T q)          -> dw_gu [2F,K]
       fp8_gemm_dgrad_t(dGUq, W_gu^T)          -> dxn [T,K]    (gradient of the RMSNorm output)
+      fp8_rmsnorm_bwd(x, gamma, rstd, dxn)    -> dx [T,K], dgamma [K]   (when x and gamma are given)
 
     dy bf16 [T,K]; saved is the dict returned by fp8_mlp_fwd; wguT/sguT and
     wdT/sdT are the transposed weight copies (fp8_weight_transpose of the
     fused gate/up and down weights).  T % 128 == 0 (WGrad groups run along T).
-    Returns dict(dxn, dw_gu, dw_down, dh)."""
+    x, gamma: the block's input and RMSNorm gain (the forward's arguments);
+    with them the RMSNorm backward runs too.
+    Returns dict(dxn, dw_gu, dw_down, dh[, dx, dgamma])."""
     T, K = dy.shape
     F = saved["hq"].shape[1]
     st = stream
@@ -497,7 +537,10 @@ def fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, stream=None):
     xTq, sxT = fp8_quant_transpose(saved["xq"], saved["sx"], stream=st)
     dw_gu = fp8_gemm_wgrad(dguTq, sguT_, xTq, sxT, stream=st)
     dxn = fp8_gemm_dgrad_t(dguq, sdgu, wguT, sguT, stream=st)
-    return {"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh}
+    grads = {"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh}
+    if x is not None and gamma is not None:
+        grads["dx"], grads["dgamma"] = fp8_rmsnorm_bwd(x, gamma, saved["rstd"], dxn, stream=st)
+    return grads
 
 
 def fp8_gemm_dgrad(dyq, sdy, wq, sw, out=None, stream=None):

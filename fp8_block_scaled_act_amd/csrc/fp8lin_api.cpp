@@ -487,6 +487,42 @@ fp8lin_status fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int
     return end_launch();
 }
 
+int64_t fp8_rmsnorm_bwd_workspace(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 0 || K % kGroup != 0 || K > 16384)
+        return -1;
+    int64_t b;
+    if (!bytes_of((M + kGroup - 1) / kGroup, K, 8, &b))
+        return -1;
+    return b;
+}
+
+fp8lin_status fp8_rmsnorm_bwd(const void* x, const void* gamma, const float* rstd, const void* dy, int64_t M,
+                              int64_t K, void* dx, float* dgamma, double* workspace, int64_t workspace_bytes,
+                              void* stream)
+{
+    const int64_t need = fp8_rmsnorm_bwd_workspace(M, K);
+    if (need < 0 || M > kMaxBlocks || (M + kGroup - 1) / kGroup > kMaxGridY)
+        return FP8LIN_ERR_SHAPE;
+    const int64_t wneed = dgamma ? need : 0;
+    if (workspace_bytes < wneed)
+        return FP8LIN_ERR_ARG;
+    int64_t bx, bg, br, bdg;
+    if (!bytes_of(M, K, 2, &bx) || !bytes_of(K, 1, 2, &bg) || !bytes_of(M, 1, 4, &br) || !bytes_of(K, 1, 4, &bdg))
+        return FP8LIN_ERR_SHAPE;
+    if (bx == 0)
+        return FP8LIN_OK;
+    const Buf in[] = {{x, bx}, {gamma, bg}, {rstd, br}, {dy, bx}};
+    const Buf out[] = {{dx, bx}, {dgamma, dgamma ? bdg : 0}, {workspace, wneed}};
+    fp8lin_status s = check_buffers(in, 4, out, 3);
+    if (s != FP8LIN_OK)
+        return s;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_rmsnorm_bwd(x, gamma, rstd, dy, M, K, dx, dgamma, workspace, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M, int64_t F,
                                uint8_t* hq, float* sh, void* stream)
 {

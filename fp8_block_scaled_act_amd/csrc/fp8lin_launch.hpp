@@ -21,6 +21,9 @@ void launch_decode_probe(const uint8_t* in, int64_t n, float* out, int method, h
 // Producer operators fused with 1x128 quantization (K <= 16384 for RMSNorm).
 void launch_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int64_t K, float eps, uint8_t* q,
                           float* s, float* rstd, hipStream_t st);
+// RMSNorm backward: dx, and dgamma (when non-NULL) through ws [ceil(M/128)][K] fp64.
+void launch_rmsnorm_bwd(const void* x, const void* gamma, const float* rstd, const void* dy, int64_t M, int64_t K,
+                        void* dx, float* dgamma, double* ws, hipStream_t st);
 void launch_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M, int64_t F, uint8_t* q,
                          float* s, hipStream_t st);
 void launch_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void* dh, int64_t M, int64_t F,

@@ -202,6 +202,145 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     }
 }
 
+// ======================================================= RMSNorm backward
+//
+// y = x r gamma with r the forward's rstd (y's rounding passed straight
+// through): dx_j = r g_j - x_j r^3 c / K with g_j = gamma_j dy_j and
+// c = sum_i g_i x_i; dgamma_k = sum_t dy[t,k] x[t,k] r_t.  All in fp64 in a
+// fixed order, so every bit is determined: g and g x are exact; c follows the
+// forward's order for the sum of squares (a balanced tree over each 128-group
+// by DPP exchanges, groups ascending through lane reads);
+// dx_j = bf16(r g_j - x_j (((r r) r) (c / K))) with one rounding.  dgamma:
+// each workgroup of the second kernel adds 128 tokens of 512 columns in
+// ascending order, one fp64 accumulator per column, into the caller's
+// workspace [ceil(M/128)][K]; the third adds those block sums in ascending
+// order and rounds to fp32.
+// One workgroup of 256 threads per row: thread t holds elements
+// [2048 i + 8 t, +8) of pass i (NP passes, K <= 2048 NP) of x, dy and gamma;
+// each 16-lane group reduces its 128-group by DPP and parks the sum in LDS,
+// and every thread then adds the group sums in ascending order.
+template <int NP>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_dx_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ gamma,
+                                                             const float* __restrict__ rstd,
+                                                             const uint16_t* __restrict__ dy, int K,
+                                                             uint16_t* __restrict__ dx)
+{
+    __shared__ double gsum[128];
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int G = K >> 7;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+    const uint4* dr = reinterpret_cast<const uint4*>(dy + row * K);
+    const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+    uint4 xv[NP], dv[NP], gv[NP];
+    bool live[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        live[i] = 2048 * i + 8 * tid < K;                   // uniform over each 16-lane group
+        const int c = live[i] ? 256 * i + tid : tid & 15;   // past the end: a valid address, zeroed
+        xv[i] = load_nt(xr + c);
+        dv[i] = load_nt(dr + c);
+        gv[i] = gr[c];
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        if (!live[i])
+            dv[i] = make_uint4(0, 0, 0, 0);
+        const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+        const uint32_t gw[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+        double p[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[2 * j] = ((double)bf16_lo(gw[j]) * (double)bf16_lo(dw[j])) * (double)bf16_lo(xw[j]);
+            p[2 * j + 1] = ((double)bf16_hi(gw[j]) * (double)bf16_hi(dw[j])) * (double)bf16_hi(xw[j]);
+        }
+        const double t = sum_over_16_lanes(((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        if (live[i] && (tid & 15) == 0)
+            gsum[16 * i + (tid >> 4)] = t;
+    }
+    __syncthreads();
+    double c = 0.0;
+    for (int g = 0; g < G; ++g)
+        c = c + gsum[g];
+    const double r = (double)rstd[row];
+    const double kk = ((r * r) * r) * (c / (double)K);
+    uint4* out = reinterpret_cast<uint4*>(dx + row * K);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        const uint32_t dw[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+        const uint32_t gw[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double glo = (double)bf16_lo(gw[j]) * (double)bf16_lo(dw[j]);
+            const double ghi = (double)bf16_hi(gw[j]) * (double)bf16_hi(dw[j]);
+            const uint32_t lo = f64_to_bf16_rne(r * glo - (double)bf16_lo(xw[j]) * kk);
+            const uint32_t hi = f64_to_bf16_rne(r * ghi - (double)bf16_hi(xw[j]) * kk);
+            o[j] = lo | (hi << 16);
+        }
+        if (live[i])
+            out[256 * i + tid] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// Block sums of dgamma: workgroup (bx, by) owns columns [512 bx, +512) (two
+// per thread) and tokens [128 by, +128) (fewer in a last block), summed in
+// ascending order.
+__global__ __launch_bounds__(256) void rmsnorm_bwd_dgamma_partial_kernel(const uint16_t* __restrict__ x,
+                                                                         const float* __restrict__ rstd,
+                                                                         const uint16_t* __restrict__ dy,
+                                                                         int64_t M, int64_t K,
+                                                                         double* __restrict__ ws)
+{
+    const int64_t col = (int64_t)blockIdx.x * 512 + 2 * threadIdx.x;
+    if (col >= K)
+        return;
+    const int64_t t0 = (int64_t)blockIdx.y * kGroup;
+    const int64_t t1 = t0 + kGroup < M ? t0 + kGroup : M;
+    double a0 = 0.0, a1 = 0.0;
+    int64_t t = t0;
+    for (; t + 8 <= t1; t += 8) {                            // 8 tokens' loads in flight
+        uint32_t xw[8], dw[8];
+        float rs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            xw[u] = *reinterpret_cast<const uint32_t*>(x + (t + u) * K + col);
+            dw[u] = *reinterpret_cast<const uint32_t*>(dy + (t + u) * K + col);
+            rs[u] = rstd[t + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a0 = a0 + ((double)bf16_lo(dw[u]) * (double)bf16_lo(xw[u])) * (double)rs[u];
+            a1 = a1 + ((double)bf16_hi(dw[u]) * (double)bf16_hi(xw[u])) * (double)rs[u];
+        }
+    }
+    for (; t < t1; ++t) {
+        const uint32_t xw = *reinterpret_cast<const uint32_t*>(x + t * K + col);
+        const uint32_t dw = *reinterpret_cast<const uint32_t*>(dy + t * K + col);
+        const double rt = (double)rstd[t];
+        a0 = a0 + ((double)bf16_lo(dw) * (double)bf16_lo(xw)) * rt;
+        a1 = a1 + ((double)bf16_hi(dw) * (double)bf16_hi(xw)) * rt;
+    }
+    ws[(int64_t)blockIdx.y * K + col] = a0;
+    ws[(int64_t)blockIdx.y * K + col + 1] = a1;
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_bwd_dgamma_final_kernel(const double* __restrict__ ws,
+                                                                       int64_t nblocks, int64_t K,
+                                                                       float* __restrict__ dgamma)
+{
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k >= K)
+        return;
+    double total = 0.0;
+    for (int64_t b = 0; b < nblocks; ++b)
+        total = total + ws[b * K + k];
+    dgamma[k] = (float)total;
+}
+
 // ===================================================== SwiGLU -> FP8 1x128
 //
 // The reference evaluation is fp64: (g / (1 + exp(-g))) * u, rounded once to
@@ -556,6 +695,37 @@ void launch_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const
     const dim3 grid((unsigned)(F / kGroup), (unsigned)(T / kGroup));
     swiglu_bwd_quant_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up),
                                                   ld, static_cast<const uint16_t*>(dh), T, F, q, s, qT, sT);
+}
+
+}  // namespace fp8lin
+
+namespace fp8lin {
+
+template <int NP>
+static void rmsnorm_bwd_dx_launch(const uint16_t* x, const uint16_t* g, const float* r, const uint16_t* dy, int64_t M,
+                                  int K, uint16_t* dx, hipStream_t st)
+{
+    rmsnorm_bwd_dx_kernel<NP><<<(unsigned)M, 256, 0, st>>>(x, g, r, dy, K, dx);
+}
+
+void launch_rmsnorm_bwd(const void* x, const void* gamma, const float* rstd, const void* dy, int64_t M, int64_t K,
+                        void* dx, float* dgamma, double* ws, hipStream_t st)
+{
+    using Fn = void (*)(const uint16_t*, const uint16_t*, const float*, const uint16_t*, int64_t, int, uint16_t*,
+                        hipStream_t);
+    static constexpr Fn by_passes[9] = {nullptr, rmsnorm_bwd_dx_launch<1>, rmsnorm_bwd_dx_launch<2>,
+                                        rmsnorm_bwd_dx_launch<3>, rmsnorm_bwd_dx_launch<4>, rmsnorm_bwd_dx_launch<5>,
+                                        rmsnorm_bwd_dx_launch<6>, rmsnorm_bwd_dx_launch<7>, rmsnorm_bwd_dx_launch<8>};
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const uint16_t* dp = static_cast<const uint16_t*>(dy);
+    by_passes[(K + 2047) / 2048](xp, static_cast<const uint16_t*>(gamma), rstd, dp, M, (int)K,
+                                 static_cast<uint16_t*>(dx), st);
+    if (dgamma) {
+        const int64_t nb = (M + kGroup - 1) / kGroup;
+        const dim3 grid((unsigned)((K + 511) / 512), (unsigned)nb);
+        rmsnorm_bwd_dgamma_partial_kernel<<<grid, 256, 0, st>>>(xp, rstd, dp, M, K, ws);
+        rmsnorm_bwd_dgamma_final_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(ws, nb, K, dgamma);
+    }
 }
 
 }  // namespace fp8lin

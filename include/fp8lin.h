@@ -252,6 +252,32 @@ fp8lin_status fp8_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int
                                 uint8_t* xq, float* sx, float* rstd, void* stream);
 
 /*
+ * Backward of fp8_rmsnorm_quant's RMSNorm, y = x * r * gamma with r = the
+ * rstd the forward returned (the rounding of y and its quantization are
+ * passed straight through; gradients stay BF16, Jet-RL summary,
+ * "Quantization scheme").  With g = gamma * dy and c = sum_i g_i x_i:
+ *   dx[m,j]  = bf16(r g_j - x_j (((r r) r) (c / K)))      one rounding
+ *   dgamma_k = fp32(sum_t (dy[t,k] x[t,k]) r_t)
+ * in fp64; c is summed in fp8_rmsnorm_quant's order for the sum of squares
+ * (each 128-group a balanced binary tree, groups ascending); dgamma adds the
+ * tokens of each block of 128 rows in ascending order, then the blocks in
+ * ascending order.  Every output bit is fixed by these rules.
+ *   x, dy  : BF16 [M,K] (input; x the forward's input)
+ *   gamma  : BF16 [K];  rstd : float [M] (fp8_rmsnorm_quant's)
+ *   dx     : BF16 [M,K] (output)
+ *   dgamma : float [K] (output, may be NULL: then no workspace is needed)
+ *   workspace : double, fp8_rmsnorm_bwd_workspace(M, K) bytes (ceil(M/128) x K
+ *               block sums), caller-owned, contents ignored on entry; calls
+ *               sharing it must be ordered on one stream
+ * K % 128 == 0 and K <= 16384, else FP8LIN_ERR_SHAPE; workspace_bytes too
+ * small: FP8LIN_ERR_ARG.  M == 0 or K == 0 is an OK no-op (dgamma untouched).
+ */
+int64_t fp8_rmsnorm_bwd_workspace(int64_t M, int64_t K);   /* -1: invalid shape */
+fp8lin_status fp8_rmsnorm_bwd(const void* x, const void* gamma, const float* rstd, const void* dy,
+                              int64_t M, int64_t K, void* dx, float* dgamma,
+                              double* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * SwiGLU fused with the 1x128 activation quantization of its output (the
  * input of the MLP down projection).  Jet-RL summary, "Quantization scheme"
  * and "Implementation" (fused activation kernels).  The pages define no

@@ -131,7 +131,7 @@ WORKLOADS = {
                           "masters (with transposed copies), forward (RMSNorm->FP8, gate/up "
                           "GEMM, SwiGLU->FP8, down GEMM) and backward through the three linear layers (dual "
                           "transpose-quant of dY, FP8-source requant of H and X, SwiGLU backward fused with the "
-                          "dual quantization of its result, two DGrad and two WGrad GEMMs)"),
+                          "dual quantization of its result, two DGrad and two WGrad GEMMs, RMSNorm backward)"),
     "producers": Workload("producers", "producers", 8192, 14336, 4096, n_outliers(4096),
                           "8B-shaped producers fused with 1x128 quantization: RMSNorm of X[8192,4096], "
                           "SwiGLU of the gate/up halves of one [8192,2x14336] projection output"),

@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(L):
               "fp8_linear_fwd", "fp8_weight_transpose", "fp8_weight_pack", "fp8_gemm_fwd_packed", "fp8_gemm_dgrad",
               "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
               "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed_splitk",
-              "fp8_gemm_fwd_packed_splitk_workspace", "fp8_swiglu_bwd_quant", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_gemm_fwd_packed_splitk_workspace", "fp8_swiglu_bwd_quant", "fp8_rmsnorm_bwd",
+              "fp8_rmsnorm_bwd_workspace", "fp8lin_status_string", "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -265,6 +266,24 @@ def test_swiglu_bwd_quant_validation(L):
     assert L.fp8_swiglu_bwd_quant(A, B, 256, C, 128, 256, D, E, D + 64, A + 2 ** 26, s0) == ALIAS
     assert L.fp8_swiglu_bwd_quant(None, None, 256, None, 0, 256, None, None, None, None, s0) == OK
     assert L.fp8_swiglu_bwd_quant(A, B, 256, C, 128, 256, D, E, F, A + 2 ** 26, s0) == DEVICE
+
+
+@fake_ptrs
+def test_rmsnorm_bwd_validation(L):
+    # x, gamma, rstd, dy, M, K, dx, dgamma, ws, ws_bytes
+    need = L.fp8_rmsnorm_bwd_workspace(300, 256)
+    assert need == 3 * 256 * 8
+    assert L.fp8_rmsnorm_bwd_workspace(4, 100) == -1
+    P = [0x10000000 * (i + 1) for i in range(10)]
+    x, g, r, dy, dx, dg, ws = P[:7]
+    assert L.fp8_rmsnorm_bwd(x, g, r, dy, 300, 100, dx, dg, ws, need, s0) == SHAPE
+    assert L.fp8_rmsnorm_bwd(x, g, r, dy, 300, 256, dx, dg, ws, need - 8, s0) == ARG
+    assert L.fp8_rmsnorm_bwd(x, g, r, dy, 300, 256, dx, None, None, 0, s0) == DEVICE   # no dgamma: no workspace
+    assert L.fp8_rmsnorm_bwd(x, g, None, dy, 300, 256, dx, dg, ws, need, s0) == NULL
+    assert L.fp8_rmsnorm_bwd(x, g, r, dy, 300, 256, x + 64, dg, ws, need, s0) == ALIAS
+    assert L.fp8_rmsnorm_bwd(x, g, r, dy, 300, 256, dx, dg, ws + 4, need, s0) == ALIGN
+    assert L.fp8_rmsnorm_bwd(None, None, None, None, 0, 256, None, None, None, 0, s0) == OK
+    assert L.fp8_rmsnorm_bwd(x, g, r, dy, 300, 256, dx, dg, ws, need, s0) == DEVICE
 
 
 @fake_ptrs

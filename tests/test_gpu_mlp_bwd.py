@@ -149,7 +149,10 @@ def oracle_block_fwd_bwd(x, gamma, wgu, wdown, dy, eps):
     xTq, sxT = oracle.quant_transpose_fp8(xq, sx)
     dw_gu = oracle.gemm_wgrad(dguTq, sdguT, xTq, sxT)
     dxn = oracle.gemm_dgrad(dguq, sdgu, owgu, osgu)
-    return {"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh, "dgu": dgu}, (owgu, osgu, owd, osd)
+    _, rstd = oracle.rmsnorm_bf16(x, gamma, eps)
+    dx, dgamma = oracle.rmsnorm_bwd(x, gamma, rstd, oracle.f64_to_bf16(dxn))
+    return ({"dxn": dxn, "dw_gu": dw_gu, "dw_down": dw_down, "dh": dh, "dgu": dgu, "dx": dx, "dgamma": dgamma},
+            (owgu, osgu, owd, osd))
 
 
 @pytest.mark.parametrize("T,K,F", [(256, 256, 384), (384, 512, 256)])
@@ -167,11 +170,13 @@ def test_mlp_backward_chain_small(T, K, F):
     saved = fl.fp8_mlp_fwd(bf16_to_dev(x), bf16_to_dev(gamma), wgu_q, sgu, wd_q, sd, eps=eps)
     wguT, sguT = fl.fp8_weight_transpose(wgu_q, sgu)
     wdT, sdT = fl.fp8_weight_transpose(wd_q, sd)
-    grads = fl.fp8_mlp_bwd(bf16_to_dev(dy), saved, wguT, sguT, wdT, sdT)
+    grads = fl.fp8_mlp_bwd(bf16_to_dev(dy), saved, wguT, sguT, wdT, sdT, x=bf16_to_dev(x),
+                           gamma=bf16_to_dev(gamma))
     errs = {}
-    for k in ("dh", "dxn", "dw_gu", "dw_down"):
+    for k in ("dh", "dxn", "dw_gu", "dw_down", "dx"):
         want = ref[k] if ref[k].dtype == np.float64 else bf16_bits_to_f64(ref[k])
         errs[k] = rms_rel(bf16_bits_to_f64(host(grads[k])), want)
+    errs["dgamma"] = rms_rel(host(grads["dgamma"]).astype(np.float64), ref["dgamma"].astype(np.float64))
     print("[mlp bwd %dx%dx%d] rms-relative errors %s" % (T, K, F, errs))
     assert max(errs.values()) <= TOL, errs
 

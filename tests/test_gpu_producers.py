@@ -166,3 +166,33 @@ def test_swiglu_quant_degenerate():
     z = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
     q, s = fl.fp8_swiglu_quant(z, z)
     assert q.shape == (0, 256) and s.shape == (0, 2)
+
+
+# -------------------------------------------------------- RMSNorm backward
+
+def run_rmsnorm_bwd(M, K, seed, what, with_dgamma=True):
+    x = synthetic.activations(M, K, seed=seed, n_out=max(1, K // 1024))
+    gamma = synthetic.norm_weights(K, seed=seed)
+    dy = synthetic.grad_out(M, K, seed=seed, sigma=1.0)
+    _, rstd = oracle.rmsnorm_bf16(x, gamma, 1e-6)           # the forward's rstd (oracle-made input)
+    odx, odg = oracle.rmsnorm_bwd(x, gamma, rstd, dy)
+    say("rmsnorm_bwd", what, M, K)
+    dx, dg = fl.fp8_rmsnorm_bwd(bf16_to_dev(x), bf16_to_dev(gamma), torch.from_numpy(rstd).to(DEV), bf16_to_dev(dy),
+                                dgamma=with_dgamma)
+    assert_same(host(dx), odx, what + " dx")
+    if with_dgamma:
+        assert_same(host(dg).view(np.uint32), odg.view(np.uint32), what + " dgamma")
+    else:
+        assert dg is None
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (130, 1024), (300, 4096), (9, 5120), (3, 3584),
+                                 (129, 16384)])
+def test_rmsnorm_bwd_shapes(M, K):
+    """dx and dgamma bit-exact: every pass count, K not a multiple of 2048,
+    token counts that leave a short last block of 128."""
+    run_rmsnorm_bwd(M, K, M + K, "%dx%d" % (M, K), with_dgamma=(M != 9))
+
+
+def test_rmsnorm_bwd_full_size():
+    run_rmsnorm_bwd(8192, 4096, 0, "8B hidden")
