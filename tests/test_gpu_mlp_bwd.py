@@ -220,3 +220,55 @@ def test_mlp_backward_8B_sampled_rows():
     for k in ("dw_gu", "dw_down"):
         w = bf16_bits_to_f64(host(grads[k]))
         assert np.all(np.isfinite(w)) and np.sqrt(np.mean(w * w)) > 0, k
+
+
+def test_mlp_train_step_graph_replays():
+    """The block's forward and backward, the split-K decode GEMM and the RMSNorm
+    backward captured in one HIP graph: every replay (new inputs, eager work
+    between replays) equals the eager calls bit for bit."""
+    T, K, F = 256, 512, 512                                     # F % 256 == 0 for the decode layout
+    owgu, osgu = oracle.quant_weight(synthetic.weights(2 * F, K, seed=3))
+    owd, osd = oracle.quant_weight(synthetic.weights(K, F, seed=4))
+    wgu_q, sgu, wd_q, sd = u8_to_dev(owgu), f32_to_dev(osgu), u8_to_dev(owd), f32_to_dev(osd)
+    wguT, sguT = fl.fp8_weight_transpose(wgu_q, sgu)
+    wdT, sdT = fl.fp8_weight_transpose(wd_q, sd)
+    wdp = fl.fp8_weight_pack(wd_q)
+    gamma = bf16_to_dev(synthetic.norm_weights(K, seed=3))
+    x = bf16_to_dev(synthetic.activations(T, K, seed=3))
+    dy = bf16_to_dev(synthetic.grad_out(T, K, seed=3))
+    hq64 = torch.empty((64, F), dtype=torch.uint8, device=DEV)
+    sh64 = torch.empty((64, F // G), dtype=torch.float32, device=DEV)
+    wsk = torch.empty((max(fl.fp8_gemm_fwd_packed_splitk_workspace(64, K, F) // 4, 1),), dtype=torch.float32,
+                      device=DEV)
+
+    def step():
+        saved = fl.fp8_mlp_fwd(x, gamma, wgu_q, sgu, wd_q, sd)
+        grads = fl.fp8_mlp_bwd(dy, saved, wguT, sguT, wdT, sdT, x=x, gamma=gamma)
+        hq64.copy_(saved["hq"][:64])
+        sh64.copy_(saved["sh"][:64])
+        ydec = fl.fp8_gemm_fwd_packed_splitk(hq64, sh64, wdp, sd, workspace=wsk)
+        return [saved["y"], saved["gu"], saved["hq"], grads["dxn"], grads["dw_gu"], grads["dw_down"],
+                grads["dx"], grads["dgamma"], ydec]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("mlp train step graph capture")
+    with torch.cuda.stream(s):
+        step()                                                  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        outs = step()
+    for r in range(3):
+        x.copy_(bf16_to_dev(synthetic.activations(T, K, seed=60 + r)))
+        dy.copy_(bf16_to_dev(synthetic.grad_out(T, K, seed=60 + r)))
+        torch.cuda.synchronize()
+        say("mlp train step graph replay", r)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t).copy() for t in outs]
+        want = [host(t) for t in step()]
+        for i, (a, b) in enumerate(zip(got, want)):
+            bad = first_mismatch(a.view(np.uint8), b.view(np.uint8))
+            assert bad is None, "replay %d output %d: %s" % (r, i, bad)
