@@ -669,10 +669,6 @@ void launch_swiglu_quant(const void* gate, const void* up, int64_t ld, int64_t M
         reinterpret_cast<uint2*>(q), s);
 }
 
-}  // namespace fp8lin
-
-namespace fp8lin {
-
 void launch_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void* dh, int64_t M, int64_t F,
                        void* dgu, hipStream_t st)
 {
@@ -685,10 +681,6 @@ void launch_swiglu_bwd(const void* gate, const void* up, int64_t ld, const void*
         F, nchunks, static_cast<uint16_t*>(dgu));
 }
 
-}  // namespace fp8lin
-
-namespace fp8lin {
-
 void launch_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const void* dh, int64_t T, int64_t F,
                              uint8_t* q, float* s, uint8_t* qT, float* sT, hipStream_t st)
 {
@@ -696,10 +688,6 @@ void launch_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const
     swiglu_bwd_quant_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up),
                                                   ld, static_cast<const uint16_t*>(dh), T, F, q, s, qT, sT);
 }
-
-}  // namespace fp8lin
-
-namespace fp8lin {
 
 template <int NP>
 static void rmsnorm_bwd_dx_launch(const uint16_t* x, const uint16_t* g, const float* r, const uint16_t* dy, int64_t M,
