@@ -902,6 +902,20 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_kernel(const GemmA
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[xt][r] = 0.f;
+        // acc += t * s, one scale per 32-row half
+        auto promote = [&](const v16f (&t)[2], const float (&sc)[2]) {
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[xt][r] = fmaf(t[xt][r], sc[xt], acc[xt][r]);
+        };
+        // unrolled loop: chunk c's partial products are scaled into acc while
+        // chunk c + 1 is multiplied (the same additions in the same order), so
+        // the promotion overlaps the next chunk's LDS reads and MFMAs instead
+        // of waiting on the last MFMA before each barrier
+        v16f prev[2];
+        float sprev[2] = {0.f, 0.f};
         __syncthreads();                           // chunk 0 of X landed, table built
         constexpr int kUnroll = NCH > 0 ? NCH : 1;
 #pragma unroll kUnroll
@@ -913,6 +927,10 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_kernel(const GemmA
 #pragma unroll
                 for (int xt = 0; xt < 2; ++xt)
                     xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
+            float sc[2];
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+                sc[xt] = lds_ps[(32 * xt + m) * GP + c * CH + kp];
             v8h wlo[2], whi[2];
             if constexpr (NCH == 0) {
                 // run-time loop: convert this chunk's W fragments before the
@@ -934,6 +952,10 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_kernel(const GemmA
             }
             if constexpr (NCH == 0)
                 __builtin_amdgcn_sched_barrier(0);
+            if constexpr (NCH > 0) {
+                if (c > 0)
+                    promote(prev, sprev);
+            }
             v16f tmp[2];
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt)
@@ -953,15 +975,19 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_kernel(const GemmA
                     tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(whi[q], xhi, tmp[xt], 0, 0, 0);
                 }
             }
+            if constexpr (NCH > 0) {
 #pragma unroll
-            for (int xt = 0; xt < 2; ++xt) {
-                const float sc = lds_ps[(32 * xt + m) * GP + c * CH + kp];
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[xt][r] = fmaf(tmp[xt][r], sc, acc[xt][r]);
+                for (int xt = 0; xt < 2; ++xt) {
+                    prev[xt] = tmp[xt];
+                    sprev[xt] = sc[xt];
+                }
+            } else {
+                promote(tmp, sc);
             }
             __syncthreads();                       // chunk c drained, chunk c + 1 landed
         }
+        if constexpr (NCH > 0)
+            promote(prev, sprev);                  // the last chunk
         __syncthreads();                           // the loader drained: the X ring is idle
         decode_reduce_store(p, acc, reinterpret_cast<float*>(&lds_x[0][0]), n0, ct, kp, kq, m, kh, lane);
     } else {
