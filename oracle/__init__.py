@@ -68,11 +68,16 @@ def lib() -> ctypes.CDLL:
         L.oracle_swiglu_bf16.argtypes = [u16p, u16p, i64, i64, i64, u16p, u8p]
         L.oracle_swiglu_bwd_bf16.argtypes = [u16p, u16p, u16p, i64, i64, i64, u16p, u8p]
         L.oracle_rmsnorm_bwd.argtypes = [u16p, u16p, f32p, u16p, i64, i64, u16p, f32p]
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_mxfp4_quant.argtypes = [u16p, i64, i64, u8p, u8p]
+        L.oracle_dequant_mxfp4.argtypes = [u8p, u8p, i64, i64, f64p]
         L.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_quant_act", "oracle_quant_weight", "oracle_quant_transpose_bf16",
                   "oracle_quant_transpose_fp8", "oracle_dequant_rowgroup",
                   "oracle_dequant_block", "oracle_gemm", "oracle_rmsnorm_bf16",
-                  "oracle_swiglu_bf16", "oracle_swiglu_bwd_bf16", "oracle_rmsnorm_bwd"):
+                  "oracle_swiglu_bf16", "oracle_swiglu_bwd_bf16", "oracle_rmsnorm_bwd",
+                  "oracle_mxfp4_quant", "oracle_dequant_mxfp4"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -321,6 +326,49 @@ def gemm_metric(c_gpu: np.ndarray, c_ref: np.ndarray, rms_ref: float | None = No
     with np.errstate(invalid="ignore", divide="ignore"):
         r = np.where(num == 0, 0.0, num / den)
     return float(np.max(r))
+
+
+# ------------------------------------------------------ 4-bit weights (MXFP4)
+
+MX_BLOCK = 32
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """fp64 values of 4-bit E2M1 codes (0..15)."""
+    L = lib()
+    table = np.array([L.oracle_e2m1_decode(i) for i in range(16)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def mxfp4_quant(w_bf16: np.ndarray):
+    """MXFP4 weight quant (OCP MX v1.0 reading of QeRL's 4-bit weights):
+    w [N,K] bf16 bits -> (codes u8 [N,K/2], two per byte, even k in the low
+    nibble; scales u8 [N,K/32], E8M0 = E + 127)."""
+    w = _bits16(w_bf16)
+    N, K = w.shape
+    assert K % MX_BLOCK == 0
+    codes = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, K // MX_BLOCK), np.uint8)
+    lib().oracle_mxfp4_quant(_ptr(w, ctypes.c_uint16), N, K, _ptr(codes, ctypes.c_uint8),
+                             _ptr(scales, ctypes.c_uint8))
+    return codes, scales
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    N, K2 = codes.shape
+    K = 2 * K2
+    assert scales.shape == (N, K // MX_BLOCK)
+    out = np.empty((N, K), np.float64)
+    lib().oracle_dequant_mxfp4(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), N, K,
+                               _ptr(out, ctypes.c_double))
+    return out
+
+
+def gemm_fwd_w4(xq, sx, w4, s4) -> np.ndarray:
+    """4-bit-weight rollout GEMM: Y[m,n] = sum_k dec(Xq)sx * e2m1(W4) 2^E (fp64)."""
+    return gemm(dequant_rowgroup(xq, sx), dequant_mxfp4(w4, s4))
 
 
 def num_threads() -> int:

@@ -29,6 +29,10 @@
  * and SwiGLU, section "Implementation": fused activation / RMSNorm kernels),
  * whose BF16 outputs are then quantized by the 1x128 activation quantizer.
  *
+ * It also holds 4-bit MXFP4 weights for the rollout GEMM (QeRL, abstract:
+ * NVFP4 weights, read here as the OCP MX format the MI355X takes), with the
+ * GEMM on dequantized operands like the FP8 ones.
+ *
  * Every function below is pinned by a CPU test against something other than
  * itself (exhaustive brute force, closed forms, exact rationals or an
  * independent library routine), except the FP8-source transpose-quant, whose
@@ -492,6 +496,100 @@ void oracle_swiglu_bwd_bf16(const uint16_t* g, const uint16_t* u, const uint16_t
                 near_tie[m * 2 * F + f] = bf16_near_tie(d_gate);
                 near_tie[m * 2 * F + F + f] = bf16_near_tie(d_up);
             }
+        }
+}
+
+/* ------------------------------------------------ 4-bit weights (MXFP4)
+ *
+ * QeRL (arXiv 2510.11696, abstract) speeds up the rollout with 4-bit NVFP4
+ * weights plus LoRA; the page gives no format details.  NVFP4 belongs to
+ * NVIDIA's Blackwell; the MI355X converters and matrix cores take the OCP
+ * Microscaling (MX) formats, so the 4-bit weights here are MXFP4 as the OCP
+ * MX specification v1.0 defines it (the project's reading):
+ *   - element E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit, no
+ *     inf/NaN; exponent field 0 is subnormal (value 0.5 * mantissa);
+ *   - 32 consecutive elements of a weight row (along K) share one E8M0 scale
+ *     2^E, stored as the byte E + 127;
+ *   - E = floor(log2(amax)) - 2 (2 is E2M1's largest exponent), clamped to
+ *     [-127, 127]; an all-zero block takes E = -127;
+ *   - an element is the E2M1 value nearest to v / 2^E, a tie going to the
+ *     code with an even last bit; magnitudes past 6 saturate to 6; the sign
+ *     of v is kept, zero results included;
+ *   - two codes per byte, the even element of K in the low nibble.
+ */
+
+/* E2M1 value of a 4-bit code, from its fields. */
+double oracle_e2m1_decode(uint8_t c)
+{
+    const int sgn = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    const double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+    return sgn ? -mag : mag;
+}
+
+/* Nearest E2M1 code to the exact value q (ties to the even code). */
+static uint8_t e2m1_nearest(double q)
+{
+    const double a = fabs(q);
+    int best = 0;
+    double bd = a;                                   /* distance to code 0 (value 0) */
+    for (int c = 1; c < 8; ++c) {
+        const double d = fabs(a - oracle_e2m1_decode((uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(q) ? 8 : 0));
+}
+
+/* Shared exponent of a block from its amax (fp64, exact). */
+static int mx_shared_exp(double amax)
+{
+    if (amax == 0.0)
+        return -127;
+    int e;
+    frexp(amax, &e);                                 /* amax = f * 2^e, f in [0.5, 1) */
+    int E = (e - 1) - 2;
+    if (E < -127)
+        E = -127;
+    if (E > 127)
+        E = 127;
+    return E;
+}
+
+/* w [N][K] bf16 (K % 32 == 0) -> codes [N][K/2], scales [N][K/32]. */
+void oracle_mxfp4_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales)
+{
+    const int64_t B = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < B; ++b) {
+            const uint16_t* v = w + n * K + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                const double a = fabs((double)oracle_bf16_to_f32(v[i]));
+                if (a > amax)
+                    amax = a;
+            }
+            const int E = mx_shared_exp(amax);
+            scales[n * B + b] = (uint8_t)(E + 127);
+            for (int i = 0; i < 32; i += 2) {
+                const uint8_t lo = e2m1_nearest(ldexp((double)oracle_bf16_to_f32(v[i]), -E));
+                const uint8_t hi = e2m1_nearest(ldexp((double)oracle_bf16_to_f32(v[i + 1]), -E));
+                codes[n * (K / 2) + b * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+}
+
+/* out[n][k] = e2m1(code) * 2^(scale - 127), in fp64. */
+void oracle_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t byte = codes[n * (K / 2) + k / 2];
+            const uint8_t c = (k & 1) ? (byte >> 4) : (byte & 15);
+            out[n * K + k] = ldexp(oracle_e2m1_decode(c), (int)scales[n * (K / 32) + k / 32] - 127);
         }
 }
 
