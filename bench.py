@@ -62,6 +62,12 @@ def act_quant_bytes(rows, cols):
     return rows * cols * 2 + rows * cols + rows * (cols // G) * 4
 
 
+def w4_gemm_bytes(M, N, K):
+    """Algorithmic bytes of the 4-bit GEMM: FP8 X and its scales, E2M1 codes
+    (half a byte each) and E8M0 scales (one byte per 32), BF16 Y."""
+    return M * K + M * (K // G) * 4 + N * K // 2 + N * (K // 32) + M * N * 2
+
+
 def weight_quant_bytes(rows, cols):
     return rows * cols * 2 + rows * cols + (rows // G) * (cols // G) * 4
 
@@ -124,6 +130,17 @@ def build_step(name, torch, fl, synthetic):
                                                                  out=y),
                    "hbm", gemm_bytes(M, N, K, (N // G) * (K // G)))
             st.dominant = "gemm_fwd"
+        elif name == "w4_decode":
+            wbytes = N * K // 2 + N * K // 32
+            st.rotate = max(8, -(-2 * MALL_BYTES // wbytes))
+            w4s = [fl.fp8_mxfp4_quant_weight(w) for _ in range(st.rotate)]
+            torch.cuda.synchronize()
+            del w
+            st.add("quant_act", lambda i: fl.fp8_quant_act(x, out=(xq, sx)), "hbm", act_quant_bytes(M, K))
+            st.add("gemm_w4", lambda i: fl.fp8_gemm_fwd_w4(xq, sx, w4s[i % st.rotate][0], w4s[i % st.rotate][1],
+                                                            out=y),
+                   "hbm", w4_gemm_bytes(M, N, K))
+            st.dominant = "gemm_w4"
         elif name == "decode_unified":
             st.rotate = max(8, -(-2 * MALL_BYTES // (N * K)))
             wqs = [fl.fp8_quant_weight(w) for _ in range(st.rotate)]
@@ -145,6 +162,8 @@ def build_step(name, torch, fl, synthetic):
                      "weight_copies_rotated": st.rotate}
         if name == "decode":
             st.config["weight_layout"] = "decode layout (fp8_weight_pack), made with the weight quantization"
+        if name == "w4_decode":
+            st.config["weight_format"] = "MXFP4 (E2M1 codes, E8M0 scale per 32 along K), quantized once"
     elif wl.kind == "mlp":
         T, F, K = wl.M, wl.N, wl.K
         x = bf16(synthetic.activations(T, K, seed=0, n_out=wl.n_out))
@@ -346,13 +365,21 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
         rows = min(M, 64)
         x = synthetic.activations(M, K, seed=0, n_out=wl.n_out)[:rows]
         w = synthetic.weights(N, K, seed=0)
-        wq, sw = oracle.quant_weight(w)
+        if name == "w4_decode":
+            w4, s4 = oracle.mxfp4_quant(w)
 
-        def work():
-            xq, sx = oracle.quant_act(x)
-            oracle.gemm_fwd(xq, sx, wq, sw)
+            def work():
+                xq, sx = oracle.quant_act(x)
+                oracle.gemm_fwd_w4(xq, sx, w4, s4)
+        else:
+            wq, sw = oracle.quant_weight(w)
+
+            def work():
+                xq, sx = oracle.quant_act(x)
+                oracle.gemm_fwd(xq, sx, wq, sw)
         what = ("%d of %d rows of X per repetition: oracle 1x128 quantization + fp64 GEMM against "
-                "the full W (W quantized once, outside the timing)" % (rows, M))
+                "the full %sW (W quantized once, outside the timing)" % (rows, M,
+                                                                         "MXFP4 " if name == "w4_decode" else ""))
     elif wl.kind in ("mlp", "mlp_train"):
         T, F, K = wl.M, wl.N, wl.K
         rows = min(T, 8)
@@ -466,6 +493,7 @@ KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes f
     "gemm_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
     "rmsnorm_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_w4": ("w4_kernels.hip",),
 }
 
 CALIB_BYTES = 4 << 30
@@ -495,6 +523,7 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "gemm_down": None,
     "rmsnorm_quant": "rmsnorm_quant_kernel",
     "swiglu_quant": "swiglu_quant_kernel",
+    "gemm_w4": "gemm_w4_kernel",
 }
 
 
@@ -574,7 +603,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode", choices=["decode", "decode_unified", "prefill", "large", "backward", "tiny", "producers", "mlp",
+    ap.add_argument("--workload", default="decode", choices=["decode", "w4_decode", "decode_unified", "prefill", "large", "backward", "tiny", "producers", "mlp",
                              "mlp_decode", "mlp_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-eager", action="store_true",

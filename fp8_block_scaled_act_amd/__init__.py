@@ -24,6 +24,7 @@ __all__ = [
     "fp8_gemm_fwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed",
     "fp8_gemm_fwd_packed_splitk", "fp8_gemm_fwd_packed_splitk_workspace", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
     "fp8_rmsnorm_quant", "fp8_rmsnorm_bwd", "fp8_rmsnorm_bwd_workspace", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_swiglu_bwd_quant", "fp8_mlp_fwd", "fp8_mlp_bwd",
+    "fp8_mxfp4_quant_weight", "fp8_gemm_fwd_w4",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
@@ -74,6 +75,9 @@ _SYMBOLS = {
                               ctypes.c_int64] + [ctypes.c_void_p] * 5, ctypes.c_int),
     "fp8_mlp_fwd": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float] + [ctypes.c_void_p] * 4 +
                     [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 8, ctypes.c_int),
+    "fp8_mxfp4_quant_weight": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "fp8_gemm_fwd_w4": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8lin_encode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
                            ctypes.c_int),
     "fp8lin_decode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
@@ -241,6 +245,40 @@ def fp8_gemm_fwd(xq, sx, wq, sw, out=None, stream=None):
     _expect(y, "y", torch.bfloat16, (M, N))
     _check(lib().fp8_gemm_fwd(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _stream(stream)),
            "fp8_gemm_fwd")
+    return y
+
+
+MX_BLOCK = 32
+
+
+def fp8_mxfp4_quant_weight(w: torch.Tensor, out=None, stream=None):
+    """MXFP4 quantization of 4-bit rollout weights: w bf16 [N,K] -> (codes u8
+    [N,K/2], two E2M1 codes per byte with the even k in the low nibble; scales
+    u8 [N,K/32], E8M0 per 32-block)."""
+    N, K = w.shape
+    _expect(w, "w", torch.bfloat16, (N, K))
+    c, s = out if out is not None else (_empty((N, K // 2), torch.uint8, w),
+                                        _empty((N, K // MX_BLOCK), torch.uint8, w))
+    _expect(c, "codes", torch.uint8, (N, K // 2))
+    _expect(s, "scales", torch.uint8, (N, K // MX_BLOCK))
+    _check(lib().fp8_mxfp4_quant_weight(_ptr(w), N, K, _ptr(c), _ptr(s), _stream(stream)),
+           "fp8_mxfp4_quant_weight")
+    return c, s
+
+
+def fp8_gemm_fwd_w4(xq, sx, codes, scales, out=None, stream=None):
+    """Y[M,N] bf16 = X W^T from 1x128-quantized X [M,K] and MXFP4 W (codes
+    [N,K/2], scales [N,K/32])."""
+    M, K = xq.shape
+    N = codes.shape[0]
+    _expect(xq, "xq", torch.uint8, (M, K))
+    _expect(sx, "sx", torch.float32, (M, K // GROUP))
+    _expect(codes, "codes", torch.uint8, (N, K // 2))
+    _expect(scales, "scales", torch.uint8, (N, K // MX_BLOCK))
+    y = out if out is not None else _empty((M, N), torch.bfloat16, xq)
+    _expect(y, "y", torch.bfloat16, (M, N))
+    _check(lib().fp8_gemm_fwd_w4(_ptr(xq), _ptr(sx), _ptr(codes), _ptr(scales), M, N, K, _ptr(y),
+                                 _stream(stream)), "fp8_gemm_fwd_w4")
     return y
 
 

@@ -313,6 +313,58 @@ fp8lin_status fp8_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq
     return end_launch();
 }
 
+fp8lin_status fp8_mxfp4_quant_weight(const void* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
+                                     void* stream)
+{
+    if (N < 0 || K < 0 || K % 32 != 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bw, bc, bs, nb;
+    if (!bytes_of(N, K, 2, &bw) || !bytes_of(N, K / 2, 1, &bc) || !bytes_of(N, K / 32, 1, &bs))
+        return FP8LIN_ERR_SHAPE;
+    if (!mul_ok(N, K / 32, &nb) || (nb + 255) / 256 > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    const Buf in[] = {{w, bw}};
+    const Buf out[] = {{codes, bc}, {scales, bs}};
+    fp8lin_status s = check_buffers(in, 1, out, 2);
+    if (s != FP8LIN_OK)
+        return s;
+    if (bc == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_mxfp4_quant(w, N, K, codes, scales, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8_gemm_fwd_w4(const uint8_t* xq, const float* sx, const uint8_t* codes, const uint8_t* scales,
+                              int64_t M, int64_t N, int64_t K, void* y, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || K % kGroup != 0 || K > fp8lin::gemm_w4_max_k())
+        return FP8LIN_ERR_SHAPE;
+    if ((M + 63) / 64 > kMaxGridY || (N + 63) / 64 > kMaxBlocks)
+        return FP8LIN_ERR_SHAPE;
+    int64_t bx, bsx, bc, bs, by;
+    if (!bytes_of(M, K, 1, &bx) || !bytes_of(M, K / kGroup, 4, &bsx) || !bytes_of(N, K / 2, 1, &bc) ||
+        !bytes_of(N, K / 32, 1, &bs) || !bytes_of(M, N, 2, &by))
+        return FP8LIN_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        bx = bsx = bc = bs = 0;
+    const Buf in[] = {{xq, bx}, {sx, bsx}, {codes, bc}, {scales, bs}};
+    const Buf out[] = {{y, by}};
+    fp8lin_status s = check_buffers(in, 4, out, 1);
+    if (s != FP8LIN_OK)
+        return s;
+    if (by == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    if (K == 0)
+        fp8lin::launch_fill_zero_bf16(y, M * N, as_stream(stream));
+    else
+        fp8lin::launch_gemm_fwd_w4(xq, sx, codes, scales, M, N, K, y, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8_gemm_fwd_unified(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                                    int64_t M, int64_t N, int64_t K, void* y, void* stream)
 {

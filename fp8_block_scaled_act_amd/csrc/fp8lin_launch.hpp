@@ -52,4 +52,11 @@ void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, 
 void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,
                        int64_t N, int64_t K, int64_t T, void* dw, hipStream_t st);
 
+// 4-bit (MXFP4) weights: quantization (K % 32 == 0) and the rollout GEMM
+// (K % 128 == 0, K <= gemm_w4_max_k(), M, N >= 1).
+void launch_mxfp4_quant(const void* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t st);
+int64_t gemm_w4_max_k();
+void launch_gemm_fwd_w4(const uint8_t* xq, const float* sx, const uint8_t* w4, const uint8_t* s4, int64_t M,
+                        int64_t N, int64_t K, void* y, hipStream_t st);
+
 }  // namespace fp8lin

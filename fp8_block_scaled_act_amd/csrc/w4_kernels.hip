@@ -1,0 +1,295 @@
+// w4_kernels.hip -- 4-bit (MXFP4) weights for the rollout GEMM, gfx950.
+//
+// QeRL (arXiv 2510.11696, abstract) runs the rollout on 4-bit NVFP4 weights
+// and gives no format details.  NVFP4 belongs to NVIDIA's Blackwell; gfx950's
+// converters and matrix cores take the OCP Microscaling formats, so the
+// weights here are MXFP4 as OCP MX v1.0 defines it:
+//   - E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit;
+//     magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6);
+//   - 32 consecutive elements of a weight row share one E8M0 scale 2^E,
+//     stored as E + 127, with E = floor(log2(amax)) - 2 clamped to
+//     [-127, 127] (-127 for an all-zero block);
+//   - an element is the E2M1 value nearest to v / 2^E, ties to the even
+//     code, saturated at 6, sign kept; two per byte, even k in the low nibble.
+//
+// GEMM (activations keep the flow's FP8 1x128 groups):
+//     Y[m,n] = sum_g sx[m,g] * sum_{k in g} dec(X[m,k]) * e2m1(W[n,k]) * 2^E[n,k/32]
+// Both operands are converted exactly to fp16 and multiplied on the fp16
+// matrix core (gfx950's FP8 matrix core truncates inside its sums).  An E2M1
+// code is converted with its block's scale relative to the largest block
+// scale Ec of the same column and 128-group, 2^(E - Ec) <= 1: exact in fp16
+// unless the block lies more than 2^23 below that largest block (its terms
+// are then below 2^-20 of the group's largest weight).  2^Ec and sx enter the
+// fp32 promotion once per group.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8lin_launch.hpp"
+
+namespace fp8lin {
+namespace w4 {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kGroup = 128;
+constexpr int kBlock = 32;
+
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------- quantization
+
+// E2M1 magnitude code of a = |v| / 2^E (a < 8): the nearest of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even code, 6 for a > 5.
+__device__ __forceinline__ uint32_t e2m1_mag(float a)
+{
+    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+           (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+}
+
+// 4-bit code of the bf16 `bits` scaled by 2^-E (exact: a power-of-two scaling).
+__device__ __forceinline__ uint32_t e2m1_code(uint32_t bits, int negE)
+{
+    const float q = __builtin_amdgcn_ldexpf(__uint_as_float(bits << 16), negE);
+    return e2m1_mag(fabsf(q)) | (((bits >> 15) & 1u) << 3);
+}
+
+// One thread per 32-element block of W [N][K] bf16: its 16 code bytes and its
+// scale byte.
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ w, int64_t nblocks,
+                                                          int64_t bpr, int64_t K, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nblocks)
+        return;
+    const int64_t n = i / bpr, b = i - n * bpr;
+    const u32x4* src = reinterpret_cast<const u32x4*>(w + n * K + b * kBlock);
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        v[j] = __builtin_nontemporal_load(src + j);
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t lo = v[j][c] & 0x7FFFu, hi = (v[j][c] >> 16) & 0x7FFFu;
+            amax = amax > lo ? amax : lo;
+            amax = amax > hi ? amax : hi;
+        }
+    // floor(log2(amax)) = exponent field - 127 for a normal amax; zero and
+    // subnormal amax (floor(log2) <= -127) clamp to E = -127
+    const int ef = (int)(amax >> 7);
+    int E = ef == 0 ? -127 : ef - 127 - 2;
+    E = E < -127 ? -127 : (E > 127 ? 127 : E);
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t lo = e2m1_code(v[j][c] & 0xFFFFu, -E), hi = e2m1_code(v[j][c] >> 16, -E);
+            word |= (lo | (hi << 4)) << (8 * c);
+        }
+        out[j] = word;
+    }
+    *reinterpret_cast<u32x4*>(codes + n * (K / 2) + b * 16) = out;
+    scales[n * bpr + b] = (uint8_t)(E + 127);
+}
+
+// ------------------------------------------------------------------ GEMM
+
+// 8 E4M3 codes (two words, element order by byte) -> 8 fp16, exact.
+__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t a, uint32_t b)
+{
+    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)a, 1.0f, false);
+    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)a, 1.0f, true);
+    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b, 1.0f, false);
+    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b, 1.0f, true);
+    return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// 8 E2M1 codes (one word, element 2i in the low nibble of byte i) -> 8 fp16
+// times `scale` (a power of two, 2^-30 <= scale <= 1).
+__device__ __forceinline__ v8h fp4x8_to_f16(uint32_t w, float scale)
+{
+    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0);
+    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1);
+    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2);
+    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3);
+    return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// A workgroup computes 64 rows x 64 columns of Y with four waves: wave
+// (ct, kq) owns W columns [32ct, 32ct + 32) and the K half [64kq, 64kq + 64)
+// of every 128-group, for both 32-row halves of X (two 32x32 tiles).  Lane
+// (j = lane & 31, kh = lane >> 5) is A row j (an X row) and B column j (a W
+// column); its K slots in MFMA step s (0..3) are
+//     k = 128g + 64kq + 32kh + 8s + e,  e = 0..7,
+// so its 32 W elements of a group are exactly the MX block 4g + 2kq + kh.
+// The two K halves are added in a fixed order at the end.  Requires
+// K % 128 == 0, K <= kMaxK, M, N >= 1; rows past M and columns past N read the
+// last row / column and are not stored.
+constexpr int kMaxK = 16384;
+
+__global__ __launch_bounds__(256) void gemm_w4_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
+                                                      const uint8_t* __restrict__ w4,
+                                                      const uint8_t* __restrict__ s4, int64_t M, int64_t N,
+                                                      int64_t K, uint16_t* __restrict__ y)
+{
+    __shared__ __attribute__((aligned(16))) float lds_sx[kMaxK / kGroup][64];
+    __shared__ __attribute__((aligned(16))) float lds_red[2][2][16][64];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ct = wave & 1, kq = wave >> 1;
+    const int j = lane & 31, kh = lane >> 5;
+    const int64_t G = K / kGroup;
+    const int64_t n0 = (int64_t)blockIdx.x * 64, m0 = (int64_t)blockIdx.y * 64;
+
+    // lds_sx[g][r] = sx[m0 + r][g]
+    for (int64_t idx = tid; idx < 64 * G; idx += 256) {
+        const int64_t r = idx / G, g = idx - r * G;
+        const int64_t row = m0 + r < M ? m0 + r : M - 1;
+        lds_sx[g][r] = sx[row * G + g];
+    }
+
+    const int64_t col = n0 + 32 * ct + j;
+    const int64_t ccol = col < N ? col : N - 1;
+    // group g: W bytes [64g + 32kq + 16kh, +16) of the column (4 u32x4 per
+    // group), its 4 scale bytes at word g, X bytes [128g + 64kq + 32kh, +32)
+    // of the row (8 u32x4 per group)
+    const u32x4* wp = reinterpret_cast<const u32x4*>(w4 + ccol * (K / 2) + 32 * kq + 16 * kh);
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(s4 + ccol * (K / kBlock));
+    const u32x4* xp[2];
+#pragma unroll
+    for (int xt = 0; xt < 2; ++xt) {
+        const int64_t row = m0 + 32 * xt + j;
+        const int64_t crow = row < M ? row : M - 1;
+        xp[xt] = reinterpret_cast<const u32x4*>(xq + crow * K + 64 * kq + 32 * kh);
+    }
+
+    v16f acc[2];
+#pragma unroll
+    for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[xt][r] = 0.f;
+
+    u32x4 wv = __builtin_nontemporal_load(wp);
+    uint32_t sv = sp[0];
+    u32x4 xv[2][2];
+#pragma unroll
+    for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            xv[xt][h] = xp[xt][h];
+    __syncthreads();                               // scale table built
+
+    const int my_block = 2 * kq + kh;              // block 4g + my_block
+    for (int64_t g = 0; g < G; ++g) {
+        const u32x4 wc = wv;
+        const uint32_t sc = sv;
+        u32x4 xc[2][2];
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                xc[xt][h] = xv[xt][h];
+        {
+            const int64_t gn = g + 1 < G ? g + 1 : g;   // last group: a harmless re-read
+            wv = __builtin_nontemporal_load(wp + 4 * gn);
+            sv = sp[gn];
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    xv[xt][h] = xp[xt][8 * gn + h];
+        }
+        const int e0 = (int)(sc & 255u), e1 = (int)((sc >> 8) & 255u), e2 = (int)((sc >> 16) & 255u),
+                  e3 = (int)(sc >> 24);
+        const int ec = max(max(e0, e1), max(e2, e3));
+        const int eb = (int)((sc >> (8 * my_block)) & 255u);
+        const float cs = __builtin_amdgcn_ldexpf(1.0f, max(eb - ec, -30));
+        v8h wf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            wf[s] = fp4x8_to_f16(wc[s], cs);
+        v16f tmp[2];
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                tmp[xt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt) {
+                const u32x4& xw = xc[xt][s >> 1];
+                const v8h xf = fp8x8_to_f16(xw[2 * (s & 1)], xw[2 * (s & 1) + 1]);
+                tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf, wf[s], tmp[xt], 0, 0, 0);
+            }
+        // D[i][j]: register r holds X row i = 8(r/4) + 4kh + (r%4) of the tile
+        const int esh = ec - 127;
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float4 s4v = *reinterpret_cast<const float4*>(&lds_sx[g][32 * xt + 8 * a + 4 * kh]);
+                acc[xt][4 * a + 0] = fmaf(tmp[xt][4 * a + 0], __builtin_amdgcn_ldexpf(s4v.x, esh), acc[xt][4 * a + 0]);
+                acc[xt][4 * a + 1] = fmaf(tmp[xt][4 * a + 1], __builtin_amdgcn_ldexpf(s4v.y, esh), acc[xt][4 * a + 1]);
+                acc[xt][4 * a + 2] = fmaf(tmp[xt][4 * a + 2], __builtin_amdgcn_ldexpf(s4v.z, esh), acc[xt][4 * a + 2]);
+                acc[xt][4 * a + 3] = fmaf(tmp[xt][4 * a + 3], __builtin_amdgcn_ldexpf(s4v.w, esh), acc[xt][4 * a + 3]);
+            }
+    }
+
+    // K half 1 into LDS, then half 0 adds it and stores
+    if (kq == 1) {
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                lds_red[ct][xt][r][lane] = acc[xt][r];
+    }
+    __syncthreads();
+    if (kq == 0 && col < N) {
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + 32 * xt + 8 * (r >> 2) + 4 * kh + (r & 3);
+                if (row < M)
+                    y[row * N + col] = bf16_rne(acc[xt][r] + lds_red[ct][xt][r][lane]);
+            }
+    }
+}
+
+}  // namespace w4
+
+// ---------------------------------------------------------- launchers
+
+void launch_mxfp4_quant(const void* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t st)
+{
+    const int64_t bpr = K / w4::kBlock, nblocks = N * bpr;
+    const unsigned grid = (unsigned)((nblocks + 255) / 256);
+    w4::quant_mxfp4_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(w), nblocks, bpr, K, codes, scales);
+}
+
+int64_t gemm_w4_max_k() { return w4::kMaxK; }
+
+void launch_gemm_fwd_w4(const uint8_t* xq, const float* sx, const uint8_t* w4c, const uint8_t* s4, int64_t M,
+                        int64_t N, int64_t K, void* y, hipStream_t st)
+{
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    w4::gemm_w4_kernel<<<grid, 256, 0, st>>>(xq, sx, w4c, s4, M, N, K, static_cast<uint16_t*>(y));
+}
+
+}  // namespace fp8lin

@@ -447,6 +447,43 @@ fp8lin_status fp8_gemm_wgrad(const uint8_t* dyTq, const float* sdyT,
                              void* dw, void* stream);
 
 /*
+ * 4-bit weights for the rollout GEMM: MXFP4 quantization of BF16 weights
+ * (once per optimizer step).  QeRL (arXiv 2510.11696, abstract) runs the
+ * rollout on 4-bit NVFP4 weights without giving the format; it is read here
+ * as OCP MX v1.0 MXFP4, the 4-bit format gfx950 converts natively:
+ *   w      : BF16 [N,K]                (input)
+ *   codes  : uint8 [N][K/2]            (output) E2M1 codes, two per byte, the
+ *            even k in the low nibble (sign bit 3, exponent bits 2..1 with
+ *            bias 1, mantissa bit 0)
+ *   scales : uint8 [N][K/32]           (output) E8M0 = E + 127 per block of 32
+ *            consecutive k, E = floor(log2(amax)) - 2 clamped to [-127, 127],
+ *            -127 for an all-zero block
+ * An element is the E2M1 value nearest to w / 2^E, ties to the even code,
+ * magnitudes past 6 saturate to 6, the sign is kept.  Inputs must be finite.
+ * K % 32 == 0.  N == 0 or K == 0 is an OK no-op.
+ */
+fp8lin_status fp8_mxfp4_quant_weight(const void* w, int64_t N, int64_t K,
+                                     uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Rollout GEMM on 4-bit weights (NT):  Y = X W^T, with the activations in the
+ * flow's FP8 1x128 groups (fp8_quant_act) and W from fp8_mxfp4_quant_weight.
+ * QeRL (arXiv 2510.11696, abstract): 4-bit weights for the rollout.
+ *   Y[m,n] = sum_g sx[m][g] * sum_{k in g} dec(xq[m,k]) * e2m1(w[n,k]) * 2^E[n][k/32]
+ *   xq : [M,K], sx : [M][K/128], codes : [N][K/2], scales : [N][K/32]
+ *   y  : BF16 [M,N] (output), fp32 accumulation, round-to-nearest-even.
+ * The codes are multiplied exactly on the fp16 matrix core; a 32-block more
+ * than 2^23 below the largest block of its column's 128-group is rounded in
+ * fp16.  Any M (64-row slabs); best for M <= 64.
+ * K % 128 == 0 and K <= 16384; M, N >= 0 free.  M == 0 or N == 0 is an OK
+ * no-op; K == 0 writes zeros.
+ */
+fp8lin_status fp8_gemm_fwd_w4(const uint8_t* xq, const float* sx,
+                              const uint8_t* codes, const uint8_t* scales,
+                              int64_t M, int64_t N, int64_t K,
+                              void* y, void* stream);
+
+/*
  * Diagnostics: the device's fp32 -> E4M3 encoder and E4M3 -> fp32 decoder on n
  * values, so that tests can check them against the definition on every input
  * (all 2^32 fp32 bit patterns, all 256 codes).

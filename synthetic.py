@@ -111,6 +111,9 @@ WORKLOADS = {
                      "forward quantized linear, X[128,1024] W[1024,1024]"),
     "decode": Workload("decode", "forward", 64, 14336, 4096, n_outliers(4096),
                        "8B-shaped MLP up-proj decode step, X[64,4096] W[14336,4096] pre-quantized"),
+    "w4_decode": Workload("w4_decode", "forward", 64, 14336, 4096, n_outliers(4096),
+                          "8B-shaped MLP up-proj rollout decode step on 4-bit MXFP4 weights, X[64,4096] FP8 1x128, "
+                          "W[14336,4096] MXFP4 pre-quantized"),
     "decode_unified": Workload("decode_unified", "forward", 64, 14336, 4096, n_outliers(4096),
                                "8B-shaped MLP up-proj decode step on the unified kernel (rows bit-identical to "
                                "training-sized calls), X[64,4096] W[14336,4096] pre-quantized"),

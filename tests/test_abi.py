@@ -328,3 +328,29 @@ def test_valid_call_without_gpu_reports_device_error(L):
 def test_binding_raises_on_error(L):
     with pytest.raises(fl.Fp8LinError, match="FP8LIN_ERR_SHAPE"):
         fl._check(SHAPE, "x")
+
+
+@fake_ptrs
+def test_mxfp4_quant_weight_validation(L):
+    # w, N, K, codes, scales
+    assert L.fp8_mxfp4_quant_weight(A, 4, 100, B, C, s0) == SHAPE          # K % 32
+    assert L.fp8_mxfp4_quant_weight(A, -1, 64, B, C, s0) == SHAPE
+    assert L.fp8_mxfp4_quant_weight(A, 2 ** 62, 2 ** 20, B, C, s0) == SHAPE  # byte count overflows
+    assert L.fp8_mxfp4_quant_weight(A, 4, 64, None, C, s0) == NULL
+    assert L.fp8_mxfp4_quant_weight(A, 4, 64, B, C + 4, s0) == ALIGN
+    assert L.fp8_mxfp4_quant_weight(A, 4, 64, A + 64, C, s0) == ALIAS     # codes over w
+    assert L.fp8_mxfp4_quant_weight(None, 0, 64, None, None, s0) == OK
+    assert L.fp8_mxfp4_quant_weight(A, 4, 96, B, C, s0) == DEVICE          # K % 128 != 0 is fine here
+
+
+@fake_ptrs
+def test_gemm_fwd_w4_validation(L):
+    # xq, sx, codes, scales, M, N, K, y
+    assert L.fp8_gemm_fwd_w4(A, B, C, D, 4, 100, 96, E, s0) == SHAPE      # K % 128
+    assert L.fp8_gemm_fwd_w4(A, B, C, D, 4, 100, 16384 + 128, E, s0) == SHAPE   # K limit
+    assert L.fp8_gemm_fwd_w4(A, B, C, D, 64 * 65536, 100, 128, E, s0) == SHAPE  # grid limit
+    assert L.fp8_gemm_fwd_w4(A, B, None, D, 4, 100, 128, E, s0) == NULL
+    assert L.fp8_gemm_fwd_w4(A, B, C, D + 4, 4, 100, 128, E, s0) == ALIGN
+    assert L.fp8_gemm_fwd_w4(A, B, C, D, 4, 100, 128, C, s0) == ALIAS
+    assert L.fp8_gemm_fwd_w4(None, None, None, None, 0, 100, 128, None, s0) == OK
+    assert L.fp8_gemm_fwd_w4(A, B, C, D, 4, 100, 128, E, s0) == DEVICE    # any N
