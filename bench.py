@@ -473,27 +473,27 @@ KERNEL_SOURCES = {           # bench kernel name -> the sources its code comes f
     "quant_weight": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "quant_transpose_dual_dY": ("quant_kernels.hip", "quant_tile.hpp", "fp8lin_device.hpp"),
     "quant_transpose_fp8_X": ("quant_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_fwd": ("gemm_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_dgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_wgrad": ("gemm_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_wgrad_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_fwd": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
+    "gemm_dgrad": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
+    "gemm_wgrad": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
+    "gemm_gate_up": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
+    "gemm_wgrad_down": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
     "quant_weight_gate_up": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "quant_weight_down": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "weight_transpose_gate_up": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "weight_transpose_down": ("quant_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_dgrad_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_wgrad_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_dgrad_gate_up": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_dgrad_down": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
+    "gemm_wgrad_gate_up": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
+    "gemm_dgrad_gate_up": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
     "quant_transpose_fp8_H": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "quant_transpose_dual_dGU": ("quant_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_bwd": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "rmsnorm_bwd": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_bwd_quant": ("producer_kernels.hip", "quant_tile.hpp", "fp8lin_device.hpp"),
-    "gemm_down": ("gemm_kernels.hip", "fp8lin_device.hpp"),
+    "gemm_down": ("gemm_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
     "rmsnorm_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
     "swiglu_quant": ("producer_kernels.hip", "fp8lin_device.hpp"),
-    "gemm_w4": ("w4_kernels.hip",),
+    "gemm_w4": ("w4_kernels.hip", "decode_stream.hpp", "fp8lin_device.hpp"),
 }
 
 CALIB_BYTES = 4 << 30
@@ -523,7 +523,7 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
     "gemm_down": None,
     "rmsnorm_quant": "rmsnorm_quant_kernel",
     "swiglu_quant": "swiglu_quant_kernel",
-    "gemm_w4": "gemm_w4_kernel",
+    "gemm_w4": "gemm_w4",
 }
 
 

@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "decode_stream.hpp"
 #include "fp8lin_launch.hpp"
 
 namespace fp8lin {
@@ -272,6 +273,153 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint8_t* __restrict_
     }
 }
 
+
+// Decode form (M <= 64, K % 256 == 0): X streams through the LDS ring of the
+// FP8 decode GEMMs (wave 8, two groups per chunk, one barrier per chunk), so
+// each workgroup reads X once; waves 0-7 = (ct, kp, kq) load their W codes
+// straight into registers one chunk ahead.  Wave (ct, kp, kq) owns W columns
+// [32ct, +32) and, of each chunk, group kp and the K quarter pieces
+// {4kh + 2kq + q} of it: lane (m, kh) holds X row m of each 32-row tile and W
+// column m at k = 64kh + 32kq + 16q + e within the group -- its 32 W codes are
+// the MX block 2kh + kq of the group.  Each chunk's partial products are
+// promoted during the next chunk; the four (kp, kq) partials are added in a
+// fixed order at the end.  Rows past M read row M - 1 and are not stored.
+template <int NCH>
+__global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __restrict__ xq,
+                                                             const float* __restrict__ sx,
+                                                             const uint8_t* __restrict__ w4,
+                                                             const uint8_t* __restrict__ s4, int64_t M, int64_t N,
+                                                             int64_t K, uint16_t* __restrict__ y)
+{
+    using namespace dec;
+    constexpr int WDX = 4;
+    static_assert(WDX * WCH >= 3 * 2 * 2 * 16 * 64 * 4, "partial sums fit in the X ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_x[WDX][WCH];
+    __shared__ __attribute__((aligned(16))) float lds_sx[kMaxK / kGroup * 64];   // [g][row]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t G = K / kGroup, nch = NCH > 0 ? NCH : G / CH;
+    const int64_t n0 = (int64_t)blockIdx.x * 64;
+
+    if (wave < 8) {
+        for (int64_t idx = tid; idx < 64 * G; idx += 512) {
+            const int64_t r = idx / G, g = idx - r * G;
+            const int64_t row = r < M ? r : M - 1;
+            lds_sx[g * 64 + r] = sx[row * G + g];
+        }
+        const int ct = wave & 1, kp = (wave >> 1) & 1, kq = wave >> 2;
+        const int m = lane & 31, kh = lane >> 5;
+        const int64_t col = n0 + 32 * ct + m;
+        const int64_t ccol = col < N ? col : N - 1;
+        // chunk c: group 2c + kp, code bytes [64(2c + kp) + 32kh + 16kq, +16)
+        // of the column (8 u32x4 per chunk), scale word 2c + kp
+        const u32x4* wp = reinterpret_cast<const u32x4*>(w4 + ccol * (K / 2) + 64 * kp + 32 * kh + 16 * kq);
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(s4 + ccol * (K / kBlock)) + kp;
+        u32x4 wreg = __builtin_nontemporal_load(wp);
+        uint32_t sreg = sp[0];
+        const int my_block = 2 * kh + kq;
+
+        v16f acc[2], prev[2];
+#pragma unroll
+        for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[xt][r] = prev[xt][r] = 0.f;
+        int prev_g = 0, prev_esh = 0;
+        // acc += t * sx[row][g] * 2^esh (rows of the lane's registers)
+        auto promote = [&](const v16f (&t)[2], int g, int esh) {
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const float4 sv = *reinterpret_cast<const float4*>(&lds_sx[g * 64 + 32 * xt + 8 * a + 4 * kh]);
+                    acc[xt][4 * a + 0] = fmaf(t[xt][4 * a + 0], __builtin_amdgcn_ldexpf(sv.x, esh), acc[xt][4 * a + 0]);
+                    acc[xt][4 * a + 1] = fmaf(t[xt][4 * a + 1], __builtin_amdgcn_ldexpf(sv.y, esh), acc[xt][4 * a + 1]);
+                    acc[xt][4 * a + 2] = fmaf(t[xt][4 * a + 2], __builtin_amdgcn_ldexpf(sv.z, esh), acc[xt][4 * a + 2]);
+                    acc[xt][4 * a + 3] = fmaf(t[xt][4 * a + 3], __builtin_amdgcn_ldexpf(sv.w, esh), acc[xt][4 * a + 3]);
+                }
+        };
+        __syncthreads();                           // chunk 0 of X landed, table built
+        constexpr int kUnroll = NCH > 0 ? NCH : 1;
+#pragma unroll kUnroll
+        for (int64_t c = 0; c < nch; ++c) {
+            const uint8_t* xl = lds_x[c % WDX];
+            u32x4 xv[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt)
+                    xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
+            const u32x4 wc = wreg;
+            const uint32_t sc = sreg;
+            {
+                const int64_t cn = c + 1 < nch ? c + 1 : c;   // last chunk: a harmless re-read
+                wreg = __builtin_nontemporal_load(wp + 8 * cn);
+                sreg = sp[2 * cn];
+            }
+            if (c > 0)
+                promote(prev, prev_g, prev_esh);
+            const int e0 = (int)(sc & 255u), e1 = (int)((sc >> 8) & 255u), e2 = (int)((sc >> 16) & 255u),
+                      e3 = (int)(sc >> 24);
+            const int ec = max(max(e0, e1), max(e2, e3));
+            const int eb = (int)((sc >> (8 * my_block)) & 255u);
+            const float cs = __builtin_amdgcn_ldexpf(1.0f, max(eb - ec, -30));
+            v16f tmp[2];
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    tmp[xt][r] = 0.f;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const v8h wlo = fp4x8_to_f16(wc[2 * q], cs), whi = fp4x8_to_f16(wc[2 * q + 1], cs);
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt) {
+                    const v8h xlo = fp8x8_to_f16(xv[xt][q].x, xv[xt][q].y);
+                    const v8h xhi = fp8x8_to_f16(xv[xt][q].z, xv[xt][q].w);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xlo, wlo, tmp[xt], 0, 0, 0);
+                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xhi, whi, tmp[xt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+                prev[xt] = tmp[xt];
+            prev_g = (int)(2 * c + kp);
+            prev_esh = ec - 127;
+            __syncthreads();                       // chunk c drained, chunk c + 1 landed
+        }
+        promote(prev, prev_g, prev_esh);           // the last chunk
+        __syncthreads();                           // the loader drained: the X ring is idle
+        float* red = reinterpret_cast<float*>(&lds_x[0][0]);
+        const int part = kp * 2 + kq;
+        if (part != 0) {
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    red[(((part - 1) * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane] = acc[xt][r];
+        }
+        __syncthreads();
+        if (part == 0 && col < N) {
+#pragma unroll
+            for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = acc[xt][r];
+#pragma unroll
+                    for (int pp = 0; pp < 3; ++pp)
+                        v += red[((pp * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane];
+                    const int64_t row = 32 * xt + 8 * (r >> 2) + 4 * kh + (r & 3);
+                    if (row < M)
+                        y[row * N + col] = bf16_rne(v);
+                }
+        }
+    } else {
+        stream_operand<WDX>(xq, M, 0, K, nch, (uint32_t)(uintptr_t)&lds_x[0][0], lane);
+    }
+}
+
 }  // namespace w4
 
 // ---------------------------------------------------------- launchers
@@ -288,8 +436,17 @@ int64_t gemm_w4_max_k() { return w4::kMaxK; }
 void launch_gemm_fwd_w4(const uint8_t* xq, const float* sx, const uint8_t* w4c, const uint8_t* s4, int64_t M,
                         int64_t N, int64_t K, void* y, hipStream_t st)
 {
+    uint16_t* out = static_cast<uint16_t*>(y);
+    if (M <= 64 && K % (dec::CH * w4::kGroup) == 0) {
+        const unsigned grid = (unsigned)((N + 63) / 64);
+        if (K == 4096)
+            w4::gemm_w4_decode_kernel<16><<<grid, 576, 0, st>>>(xq, sx, w4c, s4, M, N, K, out);
+        else
+            w4::gemm_w4_decode_kernel<0><<<grid, 576, 0, st>>>(xq, sx, w4c, s4, M, N, K, out);
+        return;
+    }
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-    w4::gemm_w4_kernel<<<grid, 256, 0, st>>>(xq, sx, w4c, s4, M, N, K, static_cast<uint16_t*>(y));
+    w4::gemm_w4_kernel<<<grid, 256, 0, st>>>(xq, sx, w4c, s4, M, N, K, out);
 }
 
 }  // namespace fp8lin
