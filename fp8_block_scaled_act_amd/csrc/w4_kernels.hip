@@ -276,9 +276,11 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint8_t* __restrict_
 
 // Decode form (M <= 64, K % 256 == 0): X streams through the LDS ring of the
 // FP8 decode GEMMs (wave 8, two groups per chunk, one barrier per chunk), so
-// each workgroup reads X once; waves 0-7 = (ct, kp, kq) load their W codes
-// straight into registers one chunk ahead.  Wave (ct, kp, kq) owns W columns
-// [32ct, +32) and, of each chunk, group kp and the K quarter pieces
+// each workgroup reads X once; waves 0-7 load their W codes straight into
+// registers one chunk ahead and read the scale words from an LDS table (one
+// contiguous read of the workgroup's 64 scale rows at the start).  Wave
+// (ct, kp, kq) owns W columns [32ct, +32) and, of each chunk, group kp and the
+// K quarter pieces
 // {4kh + 2kq + q} of it: lane (m, kh) holds X row m of each 32-row tile and W
 // column m at k = 64kh + 32kq + 16q + e within the group -- its 32 W codes are
 // the MX block 2kh + kq of the group.  Each chunk's partial products are
@@ -296,6 +298,7 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
     static_assert(WDX * WCH >= 3 * 2 * 2 * 16 * 64 * 4, "partial sums fit in the X ring");
     __shared__ __attribute__((aligned(1024))) uint8_t lds_x[WDX][WCH];
     __shared__ __attribute__((aligned(16))) float lds_sx[kMaxK / kGroup * 64];   // [g][row]
+    __shared__ uint32_t lds_sw[64 * (kMaxK / kGroup + 1)];                       // [column][g], stride G + 1
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -303,10 +306,15 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
     const int64_t n0 = (int64_t)blockIdx.x * 64;
 
     if (wave < 8) {
+        // the X scales [g][row] and the workgroup's W scale words (four E8M0
+        // bytes per column and group) [column][g]; columns past N repeat N - 1
+        const int GS = (int)G + 1;
         for (int64_t idx = tid; idx < 64 * G; idx += 512) {
             const int64_t r = idx / G, g = idx - r * G;
             const int64_t row = r < M ? r : M - 1;
             lds_sx[g * 64 + r] = sx[row * G + g];
+            const int64_t wc = n0 + r < N ? n0 + r : N - 1;
+            lds_sw[r * GS + g] = reinterpret_cast<const uint32_t*>(s4 + wc * (K / kBlock))[g];
         }
         const int ct = wave & 1, kp = (wave >> 1) & 1, kq = wave >> 2;
         const int m = lane & 31, kh = lane >> 5;
@@ -315,9 +323,8 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
         // chunk c: group 2c + kp, code bytes [64(2c + kp) + 32kh + 16kq, +16)
         // of the column (8 u32x4 per chunk), scale word 2c + kp
         const u32x4* wp = reinterpret_cast<const u32x4*>(w4 + ccol * (K / 2) + 64 * kp + 32 * kh + 16 * kq);
-        const uint32_t* sp = reinterpret_cast<const uint32_t*>(s4 + ccol * (K / kBlock)) + kp;
+        const uint32_t* swl = lds_sw + (32 * ct + m) * GS + kp;   // + 2 words per chunk
         u32x4 wreg = __builtin_nontemporal_load(wp);
-        uint32_t sreg = sp[0];
         const int my_block = 2 * kh + kq;
 
         v16f acc[2], prev[2];
@@ -352,11 +359,10 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
                 for (int xt = 0; xt < 2; ++xt)
                     xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
             const u32x4 wc = wreg;
-            const uint32_t sc = sreg;
+            const uint32_t sc = swl[2 * c];
             {
                 const int64_t cn = c + 1 < nch ? c + 1 : c;   // last chunk: a harmless re-read
                 wreg = __builtin_nontemporal_load(wp + 8 * cn);
-                sreg = sp[2 * cn];
             }
             if (c > 0)
                 promote(prev, prev_g, prev_esh);
