@@ -321,7 +321,7 @@ fp8lin_status fp8_mxfp4_quant_weight(const void* w, int64_t N, int64_t K, uint8_
     int64_t bw, bc, bs, nb;
     if (!bytes_of(N, K, 2, &bw) || !bytes_of(N, K / 2, 1, &bc) || !bytes_of(N, K / 32, 1, &bs))
         return FP8LIN_ERR_SHAPE;
-    if (!mul_ok(N, K / 32, &nb) || (nb + 255) / 256 > kMaxBlocks)
+    if (!mul_ok(N, K / 8, &nb) || (nb + 255) / 256 > kMaxBlocks)     // four threads per 32-block
         return FP8LIN_ERR_SHAPE;
     const Buf in[] = {{w, bw}};
     const Buf out[] = {{codes, bc}, {scales, bs}};

@@ -62,48 +62,41 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t bits, int negE)
     return e2m1_mag(fabsf(q)) | (((bits >> 15) & 1u) << 3);
 }
 
-// One thread per 32-element block of W [N][K] bf16: its 16 code bytes and its
-// scale byte.
-__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ w, int64_t nblocks,
-                                                          int64_t bpr, int64_t K, uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales)
+// Four threads per 32-element block of W [N][K] bf16 (K % 32 == 0, so the
+// blocks tile the flattened array): thread i converts elements [8i, 8i + 8),
+// 16 contiguous bytes, so a wave's loads are one contiguous KB; the block's
+// amax is combined over its four lanes.  Threads past the end read the last
+// element group and store nothing (all lanes take part in the exchange).
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ w, int64_t nthreads,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nblocks)
-        return;
-    const int64_t n = i / bpr, b = i - n * bpr;
-    const u32x4* src = reinterpret_cast<const u32x4*>(w + n * K + b * kBlock);
-    u32x4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        v[j] = __builtin_nontemporal_load(src + j);
+    const bool valid = i < nthreads;
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w) + (valid ? i : nthreads - 1));
     uint32_t amax = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t lo = v[j][c] & 0x7FFFu, hi = (v[j][c] >> 16) & 0x7FFFu;
-            amax = amax > lo ? amax : lo;
-            amax = amax > hi ? amax : hi;
-        }
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t lo = v[c] & 0x7FFFu, hi = (v[c] >> 16) & 0x7FFFu;
+        amax = amax > lo ? amax : lo;
+        amax = amax > hi ? amax : hi;
+    }
+    amax = max_over_4_lanes(amax);
     // floor(log2(amax)) = exponent field - 127 for a normal amax; zero and
     // subnormal amax (floor(log2) <= -127) clamp to E = -127
     const int ef = (int)(amax >> 7);
     int E = ef == 0 ? -127 : ef - 127 - 2;
     E = E < -127 ? -127 : (E > 127 ? 127 : E);
-    u32x4 out;
+    uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t lo = e2m1_code(v[j][c] & 0xFFFFu, -E), hi = e2m1_code(v[j][c] >> 16, -E);
-            word |= (lo | (hi << 4)) << (8 * c);
-        }
-        out[j] = word;
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t lo = e2m1_code(v[c] & 0xFFFFu, -E), hi = e2m1_code(v[c] >> 16, -E);
+        word |= (lo | (hi << 4)) << (8 * c);
     }
-    *reinterpret_cast<u32x4*>(codes + n * (K / 2) + b * 16) = out;
-    scales[n * bpr + b] = (uint8_t)(E + 127);
+    if (valid) {
+        reinterpret_cast<uint32_t*>(codes)[i] = word;
+        if ((i & 3) == 0)
+            scales[i >> 2] = (uint8_t)(E + 127);
+    }
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -432,9 +425,9 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
 
 void launch_mxfp4_quant(const void* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t st)
 {
-    const int64_t bpr = K / w4::kBlock, nblocks = N * bpr;
-    const unsigned grid = (unsigned)((nblocks + 255) / 256);
-    w4::quant_mxfp4_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(w), nblocks, bpr, K, codes, scales);
+    const int64_t nthreads = N * (K / 8);
+    const unsigned grid = (unsigned)((nthreads + 255) / 256);
+    w4::quant_mxfp4_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(w), nthreads, codes, scales);
 }
 
 int64_t gemm_w4_max_k() { return w4::kMaxK; }
