@@ -110,7 +110,7 @@ def run_gemm(M, N, K, seed, what, w=None, cols=None):
 
 @pytest.mark.parametrize("M,N,K", [(1, 32, 128), (7, 100, 384), (64, 256, 4096), (65, 96, 1024),
                                    (130, 200, 512), (16, 1000, 2048), (3, 64, 16384), (1, 32, 256),
-                                   (64, 64, 256), (40, 96, 7936)])
+                                   (64, 64, 256), (40, 96, 7936), (64, 1, 512), (2, 33, 128)])
 def test_gemm_w4_shapes(M, N, K):
     """Ragged M and N, one and several 64-row slabs and 64-column blocks, K
     from one 128-group to the largest supported; M <= 64 with K % 256 == 0
