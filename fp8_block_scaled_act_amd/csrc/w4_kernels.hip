@@ -30,12 +30,11 @@
 namespace fp8lin {
 namespace w4 {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+// u32x4 (fp8lin_device.hpp), v8h and dec::cvt8 (decode_stream.hpp) are shared
+// with the FP8 kernels.
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kGroup = 128;
 constexpr int kBlock = 32;
 
 __device__ __forceinline__ uint16_t bf16_rne(float f)
@@ -100,16 +99,6 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
 }
 
 // ------------------------------------------------------------------ GEMM
-
-// 8 E4M3 codes (two words, element order by byte) -> 8 fp16, exact.
-__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t a, uint32_t b)
-{
-    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)a, 1.0f, false);
-    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)a, 1.0f, true);
-    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b, 1.0f, false);
-    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b, 1.0f, true);
-    return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
 
 // 8 E2M1 codes (one word, element 2i in the low nibble of byte i) -> 8 fp16
 // times `scale` (a power of two, 2^-30 <= scale <= 1).
@@ -228,7 +217,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint8_t* __restrict_
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt) {
                 const u32x4& xw = xc[xt][s >> 1];
-                const v8h xf = fp8x8_to_f16(xw[2 * (s & 1)], xw[2 * (s & 1) + 1]);
+                const v8h xf = dec::cvt8(xw[2 * (s & 1)], xw[2 * (s & 1) + 1]);
                 tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf, wf[s], tmp[xt], 0, 0, 0);
             }
         // D[i][j]: register r holds X row i = 8(r/4) + 4kh + (r%4) of the tile
@@ -375,8 +364,8 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
                 const v8h wlo = fp4x8_to_f16(wc[2 * q], cs), whi = fp4x8_to_f16(wc[2 * q + 1], cs);
 #pragma unroll
                 for (int xt = 0; xt < 2; ++xt) {
-                    const v8h xlo = fp8x8_to_f16(xv[xt][q].x, xv[xt][q].y);
-                    const v8h xhi = fp8x8_to_f16(xv[xt][q].z, xv[xt][q].w);
+                    const v8h xlo = dec::cvt8(xv[xt][q].x, xv[xt][q].y);
+                    const v8h xhi = dec::cvt8(xv[xt][q].z, xv[xt][q].w);
                     tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xlo, wlo, tmp[xt], 0, 0, 0);
                     tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xhi, whi, tmp[xt], 0, 0, 0);
                 }
@@ -436,7 +425,7 @@ void launch_gemm_fwd_w4(const uint8_t* xq, const float* sx, const uint8_t* w4c, 
                         int64_t N, int64_t K, void* y, hipStream_t st)
 {
     uint16_t* out = static_cast<uint16_t*>(y);
-    if (M <= 64 && K % (dec::CH * w4::kGroup) == 0) {
+    if (M <= 64 && K % (dec::CH * kGroup) == 0) {
         const unsigned grid = (unsigned)((N + 63) / 64);
         if (K == 4096)
             w4::gemm_w4_decode_kernel<16><<<grid, 576, 0, st>>>(xq, sx, w4c, s4, M, N, K, out);
