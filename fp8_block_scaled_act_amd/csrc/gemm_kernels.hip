@@ -1101,12 +1101,17 @@ __global__ __launch_bounds__(256) void pack_decode_kernel(const uint8_t* __restr
 // q ^ ((row / 2) % 8), so the 16 rows a 16-lane fragment read touches cover
 // all banks; the DMA writes eight whole rows per instruction.
 namespace nt {
-// Tile shapes: BA A rows x 128 B rows per workgroup of NW waves (WA x 2 wave
-// grid of 64 x 64 sub-tiles), D steps in flight.
-template <int BA_, int NW_, int D_>
+// Tile shapes: BA A rows x BB B rows per workgroup of NW waves, each wave a
+// TA x TB block of 32 x 32 tiles (a WA x WB wave grid), D steps in flight.
+// Every output element is computed by the same instruction sequence whatever
+// the shape (one chain of MFMAs per group in a fixed k order, then one
+// promotion), so all shapes give bit-identical results.
+template <int BA_, int NW_, int D_, int BB_ = 128, int TA_ = 2, int TB_ = 2>
 struct Cfg {
-    static constexpr int BA = BA_, BB = 128, NW = NW_, D = D_;
-    static constexpr int WA = BA / 64;             // waves along A (WA x 2 = NW)
+    static constexpr int BA = BA_, BB = BB_, NW = NW_, D = D_, TA = TA_, TB = TB_;
+    static constexpr int WA = BA / (32 * TA);      // waves along A
+    static constexpr int WB = BB / (32 * TB);      // waves along B (WA x WB = NW)
+    static constexpr int RA = BA / 64, RB = BB / 64;   // 64-row scale runs of A and of B
     static constexpr int OFF_B = BA * kGroup;
     static constexpr int OFF_SA = OFF_B + BB * kGroup;
     static constexpr int OFF_SB = OFF_SA + BA * 4;
@@ -1114,13 +1119,21 @@ struct Cfg {
     static constexpr int NA = BA / 8 / NW;         // 1 KB A-code runs per wave and step
     static constexpr int NB = BB / 8 / NW;         // 1 KB B-code runs per wave and step
     static constexpr int NDMA = NA + NB + 1;       // + one 64-row run of scales
-    static_assert(WA * 2 == NW && NA * NW * 8 == BA && NB * NW * 8 == BB, "tile / wave split");
+    static_assert(WA * WB == NW && NA * NW * 8 == BA && NB * NW * 8 == BB, "tile / wave split");
+    static_assert(RA * 64 == BA && RB * 64 == BB && NW >= RA + RB, "every scale run has a wave");
 };
 // Two workgroups per CU (2 x 66 KB of LDS): while one waits at its step
 // barrier the other computes.  Measured 5-8% ahead of one 256 x 128
 // workgroup of 8 waves with three steps in flight (Cfg<256, 8, 3>), with
 // bit-identical results.
 using Pair = Cfg<128, 4, 2>;
+// Rollout batches (M <= 64) on the batch-invariant forward: 64 x 64 tiles of
+// four waves with one 32 x 32 tile each, so an 8B up-projection fills 224
+// workgroups instead of 112 half-empty ones, four steps in flight (each wave
+// has a quarter of Pair's arithmetic per step; measured 2 / 3 / 4 / 6 / 8
+// steps: 28.5 / 23.1 / 20.8-21.9 / 24.1-24.6 / 23.6-23.8 us); bit-identical
+// to Pair.
+using Skinny = Cfg<64, 4, 4, 64, 1, 1>;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -1184,29 +1197,32 @@ __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
             const int64_t gr = n0 + row < p.N ? n0 + row : p.N - 1;
             src.b[j] = p.b + gr * p.Kc + 16 * (pos ^ ((row >> 1) & 7));
         }
-        if (wave < C::WA) {
+        if (wave < C::RA) {
             const int64_t gr = m0 + 64 * wave + lane < p.M ? m0 + 64 * wave + lane : p.M - 1;
             src.s = p.sa + gr * G;
             src.dst_s = OFF_SA + 256 * wave;
         } else {
-            // the two B-scale runs; with more waves than runs, the extra waves
+            // the B-scale runs; with more waves than runs, the extra waves
             // repeat them (same values to the same words), so that every wave
             // issues NDMA
-            const int64_t r = n0 + 64 * (wave & 1) + lane;
+            const int run = (wave - C::RA) % C::RB;
+            const int64_t r = n0 + 64 * run + lane;
             const int64_t gr = r < p.N ? r : p.N - 1;
             src.s = MODE == Mode::Fwd ? p.sb + (gr / kGroup) * G : p.sb + gr * G;
-            src.dst_s = OFF_SB + 256 * (wave & 1);
+            src.dst_s = OFF_SB + 256 * run;
         }
     }
     const uint32_t base = (uint32_t)(uintptr_t)&lds[0];
 
+    constexpr int TA = C::TA, TB = C::TB;
     const int wa = wave % C::WA, wb = wave / C::WA;
+    const int a0 = 32 * TA * wa, b0 = 32 * TB * wb;    // the wave's first A row and B row in the tile
     const int m = lane & 31, kh = lane >> 5;
-    v16f acc[2][2];
+    v16f acc[TA][TB];
 #pragma unroll
-    for (int at = 0; at < 2; ++at)
+    for (int at = 0; at < TA; ++at)
 #pragma unroll
-        for (int bt = 0; bt < 2; ++bt)
+        for (int bt = 0; bt < TB; ++bt)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[at][bt][r] = 0.f;
@@ -1224,67 +1240,73 @@ __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
         if (g + D - 1 < G)
             issue_step<C>(src, wave, base + (uint32_t)(((g + D - 1) % D) * STAGE), g + D - 1);
         const uint8_t* st = lds + (g % D) * STAGE;
-        v16f tmp[2][2];
+        v16f tmp[TA][TB];
 #pragma unroll
-        for (int at = 0; at < 2; ++at)
+        for (int at = 0; at < TA; ++at)
 #pragma unroll
-            for (int bt = 0; bt < 2; ++bt)
+            for (int bt = 0; bt < TB; ++bt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     tmp[at][bt][r] = 0.f;
         // pieces of k pair kp + 1 are read while pair kp is multiplied
-        u32x4 avn[2], bvn[2];
+        u32x4 avn[TA], bvn[TB];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            avn[t] = *reinterpret_cast<const u32x4*>(st + piece(64 * wa + 32 * t + m, kh));
-            bvn[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(64 * wb + 32 * t + m, kh));
-        }
+        for (int t = 0; t < TA; ++t)
+            avn[t] = *reinterpret_cast<const u32x4*>(st + piece(a0 + 32 * t + m, kh));
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            bvn[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(b0 + 32 * t + m, kh));
 #pragma unroll
         for (int kp = 0; kp < 4; ++kp) {
-            u32x4 av[2], bv[2];
+            u32x4 av[TA], bv[TB];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < TA; ++t)
                 av[t] = avn[t];
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
                 bv[t] = bvn[t];
-            }
             if (kp < 3) {
                 const int q = 2 * (kp + 1) + kh;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    avn[t] = *reinterpret_cast<const u32x4*>(st + piece(64 * wa + 32 * t + m, q));
-                    bvn[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(64 * wb + 32 * t + m, q));
-                }
-            }
-            v8h alo[2], ahi[2], blo[2], bhi[2];
+                for (int t = 0; t < TA; ++t)
+                    avn[t] = *reinterpret_cast<const u32x4*>(st + piece(a0 + 32 * t + m, q));
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < TB; ++t)
+                    bvn[t] = *reinterpret_cast<const u32x4*>(st + OFF_B + piece(b0 + 32 * t + m, q));
+            }
+            v8h alo[TA], ahi[TA], blo[TB], bhi[TB];
+#pragma unroll
+            for (int t = 0; t < TA; ++t) {
                 alo[t] = cvt8(av[t].x, av[t].y);
                 ahi[t] = cvt8(av[t].z, av[t].w);
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
                 blo[t] = cvt8(bv[t].x, bv[t].y);
                 bhi[t] = cvt8(bv[t].z, bv[t].w);
             }
-            // the four tiles' first k steps, then their second (a dependent
-            // pair is three instructions apart)
+            // the tiles' first k steps, then their second (with 2 x 2 tiles a
+            // dependent pair is three instructions apart)
 #pragma unroll
-            for (int at = 0; at < 2; ++at)
+            for (int at = 0; at < TA; ++at)
 #pragma unroll
-                for (int bt = 0; bt < 2; ++bt)
+                for (int bt = 0; bt < TB; ++bt)
                     tmp[at][bt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(blo[bt], alo[at], tmp[at][bt], 0, 0, 0);
 #pragma unroll
-            for (int at = 0; at < 2; ++at)
+            for (int at = 0; at < TA; ++at)
 #pragma unroll
-                for (int bt = 0; bt < 2; ++bt)
+                for (int bt = 0; bt < TB; ++bt)
                     tmp[at][bt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bhi[bt], ahi[at], tmp[at][bt], 0, 0, 0);
         }
         const float* ssa = reinterpret_cast<const float*>(st + OFF_SA);
         const float* ssb = reinterpret_cast<const float*>(st + OFF_SB);
 #pragma unroll
-        for (int at = 0; at < 2; ++at) {
-            const float sa = ssa[64 * wa + 32 * at + m];
+        for (int at = 0; at < TA; ++at) {
+            const float sa = ssa[a0 + 32 * at + m];
 #pragma unroll
-            for (int bt = 0; bt < 2; ++bt) {
+            for (int bt = 0; bt < TB; ++bt) {
                 if constexpr (MODE == Mode::Fwd) {
-                    // the tile's 128 B rows lie in one weight block
+                    // the tile's B rows lie in one 128-row weight block
                     const float s = sa * ssb[0];
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
@@ -1293,7 +1315,7 @@ __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
                     for (int a4 = 0; a4 < 4; ++a4) {
                         const f32x4 sb4 =
-                            *reinterpret_cast<const f32x4*>(ssb + 64 * wb + 32 * bt + 8 * a4 + 4 * kh);
+                            *reinterpret_cast<const f32x4*>(ssb + b0 + 32 * bt + 8 * a4 + 4 * kh);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             acc[at][bt][4 * a4 + e] = fmaf(tmp[at][bt][4 * a4 + e], sa * sb4[e],
@@ -1307,15 +1329,15 @@ __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
     // C rows are A rows (lane m of each tile), columns B rows: four
     // consecutive columns per lane and 8-byte stores (N % 4 == 0)
 #pragma unroll
-    for (int at = 0; at < 2; ++at) {
-        const int64_t row = m0 + 64 * wa + 32 * at + m;
+    for (int at = 0; at < TA; ++at) {
+        const int64_t row = m0 + a0 + 32 * at + m;
         if (row >= p.M)
             continue;
 #pragma unroll
-        for (int bt = 0; bt < 2; ++bt)
+        for (int bt = 0; bt < TB; ++bt)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
-                const int64_t col = n0 + 64 * wb + 32 * bt + 8 * a4 + 4 * kh;
+                const int64_t col = n0 + b0 + 32 * bt + 8 * a4 + 4 * kh;
                 if (col < p.N) {
                     const int r0 = 4 * a4;
                     const uint32_t v0 = (uint32_t)f32_to_bf16_rne(acc[at][bt][r0]) |
@@ -1387,9 +1409,13 @@ void launch_gemm_fwd_unified(const uint8_t* xq, const float* sx, const uint8_t* 
                              int64_t N, int64_t K, void* y, hipStream_t st)
 {
     // one kernel for every M: each output element is the same MFMA chain over
-    // the same groups in ascending order, whichever tile its row falls in
+    // the same groups in ascending order, whichever tile its row falls in and
+    // whichever tile shape (64 x 64 for rollout batches, 128 x 128 above)
     GemmArgs p{xq, sx, wq, sw, static_cast<uint16_t*>(y), M, N, K, 0, 0};
-    launch_gemm_nt<Mode::Fwd>(p, st);
+    if (M <= 64)
+        launch_gemm_nt<Mode::Fwd, nt::Skinny>(p, st);
+    else
+        launch_gemm_nt<Mode::Fwd>(p, st);
 }
 
 // Splits per 64-column block for the split-K decode GEMM: none when the
