@@ -275,6 +275,21 @@ def test_fwd_unified_rows_bitwise_across_batch_sizes():
                  "unified decode rows")
 
 
+def test_fwd_unified_bitwise_full_decode_shape():
+    """The 8B up-projection (N = 14336, K = 4096): rollout batches of 64 and 1
+    rows on the 64 x 64 tiles give the bits of a 200-row call on the 128 x 128
+    tiles."""
+    M, N, K = 200, 14336, 4096
+    xq, sx = codes_scales((M, K), (M, K // G), 7, 15)
+    wq, sw = codes_scales((N, K), (N // G, K // G), 8, 16)
+    dw, dsw = u8_to_dev(wq), f32_to_dev(sw)
+    run = lambda a, b: host(fl.fp8_gemm_fwd_unified(u8_to_dev(xq[a:b]), f32_to_dev(sx[a:b]), dw, dsw))
+    say("gemm_fwd_unified full decode shape")
+    y_all = run(0, M)
+    for a, b in ((0, 64), (64, 65), (136, 200), (199, 200)):
+        assert np.array_equal(run(a, b), y_all[a:b]), (a, b)
+
+
 @pytest.mark.parametrize("kind,M,N,K", [("fwd", 64, 14336, 4096), ("fwd", 300, 1024, 1024),
                                         ("dgrad", 300, 1024, 512), ("wgrad", 512, 384, 1024)])
 def test_gemm_deterministic(kind, M, N, K):
