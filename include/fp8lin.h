@@ -389,7 +389,9 @@ fp8lin_status fp8_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx,
 /*
  * Forward GEMM with rollout and training on one kernel: the same product as
  * fp8_gemm_fwd (same arguments, layouts, errors), computed for every M by
- * the kernel fp8_gemm_fwd uses above 64 rows.  Jet-RL summary, "Core
+ * the kernel fp8_gemm_fwd uses above 64 rows (with 64 x 64 tiles for
+ * M <= 64, whose every output element runs the same instruction sequence as
+ * in the 128 x 128 tiles).  Jet-RL summary, "Core
  * architecture": rollout must run the training forward's quantization flow
  * at the same granularity and precision; this call goes further and makes a
  * row's output bits independent of the batch it is computed in, so a
