@@ -290,13 +290,30 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
     if (wave < 8) {
         // the X scales [g][row] and the workgroup's W scale words (four E8M0
         // bytes per column and group) [column][g]; columns past N repeat N - 1
-        const int GS = (int)G + 1;
-        for (int64_t idx = tid; idx < 64 * G; idx += 512) {
-            const int64_t r = idx / G, g = idx - r * G;
-            const int64_t row = r < M ? r : M - 1;
-            lds_sx[g * 64 + r] = sx[row * G + g];
-            const int64_t wc = n0 + r < N ? n0 + r : N - 1;
-            lds_sw[r * GS + g] = reinterpret_cast<const uint32_t*>(s4 + wc * (K / kBlock))[g];
+        // four entries of each table per thread and batch, the batch's loads
+        // in flight together (a load-store loop would wait on each load)
+        const int Gi = (int)G, GS = Gi + 1, nent = 64 * Gi;
+        for (int base = 0; base < nent; base += 512 * 4) {
+            float xs[4];
+            uint32_t ws[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int idx = min(base + tid + 512 * i, nent - 1);
+                const int r = idx / Gi, g = idx - r * Gi;
+                const int64_t row = r < M ? r : M - 1;
+                const int64_t wc = n0 + r < N ? n0 + r : N - 1;
+                xs[i] = sx[row * G + g];
+                ws[i] = reinterpret_cast<const uint32_t*>(s4 + wc * (K / kBlock))[g];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int idx = base + tid + 512 * i;
+                if (idx < nent) {
+                    const int r = idx / Gi, g = idx - r * Gi;
+                    lds_sx[g * 64 + r] = xs[i];
+                    lds_sw[r * GS + g] = ws[i];
+                }
+            }
         }
         const int ct = wave & 1, kp = (wave >> 1) & 1, kq = wave >> 2;
         const int m = lane & 31, kh = lane >> 5;
