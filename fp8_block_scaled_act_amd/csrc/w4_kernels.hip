@@ -396,29 +396,62 @@ __global__ __launch_bounds__(576) void gemm_w4_decode_kernel(const uint8_t* __re
         }
         promote(prev, prev_g, prev_esh);           // the last chunk
         __syncthreads();                           // the loader drained: the X ring is idle
+        // the (kp, kq) partials through the idle X ring as 16-byte vectors,
+        // [part - 1][ct][xt][r / 4][lane][r % 4], added in a fixed order
         float* red = reinterpret_cast<float*>(&lds_x[0][0]);
         const int part = kp * 2 + kq;
+        auto red_at = [&](int pp, int xt, int a4) { return red + ((((pp * 2 + ct) * 2 + xt) * 4 + a4) * 64 + lane) * 4; };
         if (part != 0) {
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    red[(((part - 1) * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane] = acc[xt][r];
+                for (int a4 = 0; a4 < 4; ++a4)
+                    *reinterpret_cast<float4*>(red_at(part - 1, xt, a4)) =
+                        make_float4(acc[xt][4 * a4], acc[xt][4 * a4 + 1], acc[xt][4 * a4 + 2], acc[xt][4 * a4 + 3]);
         }
         __syncthreads();
-        if (part == 0 && col < N) {
+        if (part == 0) {
+            // bf16 results staged row-major in the ring past the partials
+            // ([64 rows][64 columns], this wave's 32 columns only, read back by
+            // this wave), then stored 8 columns (16 bytes) per lane
+            uint16_t* tile = reinterpret_cast<uint16_t*>(&lds_x[0][0] + 3 * 2 * 2 * 16 * 64 * 4);
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v = acc[xt][r];
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    float4 v = make_float4(acc[xt][4 * a4], acc[xt][4 * a4 + 1], acc[xt][4 * a4 + 2],
+                                           acc[xt][4 * a4 + 3]);
 #pragma unroll
-                    for (int pp = 0; pp < 3; ++pp)
-                        v += red[((pp * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane];
-                    const int64_t row = 32 * xt + 8 * (r >> 2) + 4 * kh + (r & 3);
-                    if (row < M)
-                        y[row * N + col] = bf16_rne(v);
+                    for (int pp = 0; pp < 3; ++pp) {
+                        const float4 o = *reinterpret_cast<const float4*>(red_at(pp, xt, a4));
+                        v.x += o.x;
+                        v.y += o.y;
+                        v.z += o.z;
+                        v.w += o.w;
+                    }
+                    const int row = 32 * xt + 8 * a4 + 4 * kh;
+                    const int cl = 32 * ct + m;
+                    tile[(row + 0) * 64 + cl] = bf16_rne(v.x);
+                    tile[(row + 1) * 64 + cl] = bf16_rne(v.y);
+                    tile[(row + 2) * 64 + cl] = bf16_rne(v.z);
+                    tile[(row + 3) * 64 + cl] = bf16_rne(v.w);
                 }
+            // lane L: rows L / 4 + 16 i, columns 32 ct + 8 (L % 4) .. + 8
+            const int c8 = 32 * ct + 8 * (lane & 3);
+            const int64_t gc = n0 + c8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = (lane >> 2) + 16 * i;
+                if (row >= M || gc >= N)
+                    continue;
+                const uint16_t* src = tile + row * 64 + c8;
+                if (gc + 8 <= N && (N & 7) == 0) {
+                    *reinterpret_cast<u32x4*>(y + row * N + gc) = *reinterpret_cast<const u32x4*>(src);
+                } else {
+                    for (int e = 0; e < 8 && gc + e < N; ++e)
+                        y[row * N + gc + e] = src[e];
+                }
+            }
         }
     } else {
         stream_operand<WDX>(xq, M, 0, K, nch, (uint32_t)(uintptr_t)&lds_x[0][0], lane);
