@@ -658,13 +658,16 @@ __device__ __forceinline__ void decode_scale_table(const GemmArgs& p, int64_t n0
 __device__ __forceinline__ void decode_reduce_store(const GemmArgs& p, v16f (&acc)[2], float* red, int64_t n0,
                                                     int ct, int kp, int kq, int m, int kh, int lane)
 {
+    // partials as 16-byte vectors: [part - 1][ct][xt][r / 4][lane][r % 4]
     const int part = kp * 2 + kq;
+    auto red_at = [&](int pp, int xt, int a4) { return red + ((((pp * 2 + ct) * 2 + xt) * 4 + a4) * 64 + lane) * 4; };
     if (part != 0) {
 #pragma unroll
         for (int xt = 0; xt < 2; ++xt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                red[(((part - 1) * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane] = acc[xt][r];
+            for (int a4 = 0; a4 < 4; ++a4)
+                *reinterpret_cast<v4f*>(red_at(part - 1, xt, a4)) =
+                    v4f{acc[xt][4 * a4], acc[xt][4 * a4 + 1], acc[xt][4 * a4 + 2], acc[xt][4 * a4 + 3]};
     }
     __syncthreads();
     if (part == 0) {
@@ -672,10 +675,14 @@ __device__ __forceinline__ void decode_reduce_store(const GemmArgs& p, v16f (&ac
         for (int xt = 0; xt < 2; ++xt) {
             const int64_t row = 32 * xt + m;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
-                for (int pp = 0; pp < 3; ++pp)
-                    acc[xt][r] += red[((pp * 2 + ct) * 2 + xt) * 16 * 64 + r * 64 + lane];
+                for (int pp = 0; pp < 3; ++pp) {
+                    const v4f o = *reinterpret_cast<const v4f*>(red_at(pp, xt, a4));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[xt][4 * a4 + e] += o[e];
+                }
             if (row < p.M) {
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
