@@ -7,7 +7,8 @@ weight).  fp8_gemm_fwd_w4: max|Y - Y_ref| / (|Y_ref| + 0.01 rms(Y_ref)) <= 1e-2
 against the oracle's fp64 GEMM on the same codes, over ragged M/N, several
 64-row slabs, K from one group to 4096, blocks of very different scales in one
 group, and the full decode shape on sampled columns; plus the chain GPU
-quantizers -> GPU GEMM against the oracle chain."""
+quantizers -> GPU GEMM against the oracle chain, and the rollout step
+replayed from a HIP graph."""
 import numpy as np
 import pytest
 import torch
@@ -173,3 +174,39 @@ def test_gemm_w4_degenerate():
                            torch.zeros((2, 0), dtype=torch.float32, device=DEV),
                            torch.zeros((4, 48), dtype=torch.uint8, device=DEV),
                            torch.zeros((4, 3), dtype=torch.uint8, device=DEV))
+
+
+def test_w4_rollout_step_graph_replays():
+    """The rollout step (activation quantization + 4-bit GEMM) captured in a
+    HIP graph: every replay, with eager work between replays, gives the eager
+    result bit for bit."""
+    M, N, K = 64, 2048, 4096
+    x = bf16_to_dev(synthetic.activations(M, K, seed=31, n_out=4))
+    c, s = fl.fp8_mxfp4_quant_weight(bf16_to_dev(synthetic.weights(N, K, seed=31)))
+    xq = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    sx = torch.empty((M, K // 128), dtype=torch.float32, device=DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    say("w4 graph replays", M, N, K)
+
+    def step():
+        fl.fp8_quant_act(x, out=(xq, sx))
+        fl.fp8_gemm_fwd_w4(xq, sx, c, s, out=y)
+
+    step()
+    ref = host(y).copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    for i in range(4):
+        y.zero_()
+        xq.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), ref), "replay %d" % i
