@@ -926,7 +926,7 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_kernel(const GemmA
 // ascending split order and rounds to BF16.  Deterministic, rows independent
 // of the other rows of the call; not bit-identical to the unsplit kernels
 // (the groups are added in another association).
-template <int GM>
+template <int GM, int NL = 0>
 __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_splitk_kernel(const GemmArgs p, float* ws,
                                                                             int64_t per_split)
 {
@@ -961,53 +961,117 @@ __global__ __launch_bounds__(576) void gemm_fwd_decode_packed_splitk_kernel(cons
             for (int r = 0; r < 16; ++r)
                 acc[xt][r] = 0.f;
         __syncthreads();                           // local chunk 0 of X landed, table built
-        for (int64_t lc = 0; lc < nloc; ++lc) {
-            const int64_t c = c0 + lc;
-            const uint8_t* xl = lds_x[lc % WDX];
-            u32x4 xv[2][2];
+        if constexpr (NL > 0) {
+            // every split has NL chunks: unrolled, and each chunk's partial
+            // products are scaled into acc during the next chunk (the same
+            // additions in the same order)
+            v16f prev[2];
+            float sprev[2] = {0.f, 0.f};
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int xt = 0; xt < 2; ++xt)
-                    xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
-            v8h wlo[2], whi[2];
-            // convert this chunk's W fragments before the next chunk is
-            // loaded into their registers
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                wlo[q] = cvt8(wreg[q].x, wreg[q].y);
-                whi[q] = cvt8(wreg[q].z, wreg[q].w);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            {
-                const int64_t cn = c + 1 < c1 ? c + 1 : c;   // last chunk: a harmless re-read
+            for (int lc = 0; lc < NL; ++lc) {
+                const int64_t c = c0 + lc;
+                const uint8_t* xl = lds_x[lc % WDX];
+                u32x4 xv[2][2];
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    wreg[q] = __builtin_nontemporal_load(wsrc + cn * (8 * 2 * 64) + q * 64);
+#pragma unroll
+                    for (int xt = 0; xt < 2; ++xt)
+                        xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
+                float sc[2];
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt)
+                    sc[xt] = lds_ps[(32 * xt + m) * GP + c * CH + kp];
+                const u32x4 wv[2] = {wreg[0], wreg[1]};
+                {
+                    const int64_t cn = lc + 1 < NL ? c + 1 : c;   // last chunk: a harmless re-read
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        wreg[q] = __builtin_nontemporal_load(wsrc + cn * (8 * 2 * 64) + q * 64);
+                }
+                if (lc > 0) {
+#pragma unroll
+                    for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[xt][r] = fmaf(prev[xt][r], sprev[xt], acc[xt][r]);
+                }
+                v16f tmp[2];
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        tmp[xt][r] = 0.f;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const v8h wlo = cvt8(wv[q].x, wv[q].y), whi = cvt8(wv[q].z, wv[q].w);
+#pragma unroll
+                    for (int xt = 0; xt < 2; ++xt) {
+                        const v8h xlo = cvt8(xv[xt][q].x, xv[xt][q].y), xhi = cvt8(xv[xt][q].z, xv[xt][q].w);
+                        tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wlo, xlo, tmp[xt], 0, 0, 0);
+                        tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(whi, xhi, tmp[xt], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt) {
+                    prev[xt] = tmp[xt];
+                    sprev[xt] = sc[xt];
+                }
+                __syncthreads();                   // chunk drained, the next one landed
             }
-            __builtin_amdgcn_sched_barrier(0);
-            v16f tmp[2];
 #pragma unroll
             for (int xt = 0; xt < 2; ++xt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    tmp[xt][r] = 0.f;
+                    acc[xt][r] = fmaf(prev[xt][r], sprev[xt], acc[xt][r]);
+        } else {
+            for (int64_t lc = 0; lc < nloc; ++lc) {
+                const int64_t c = c0 + lc;
+                const uint8_t* xl = lds_x[lc % WDX];
+                u32x4 xv[2][2];
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int xt = 0; xt < 2; ++xt)
+                        xv[xt][q] = *reinterpret_cast<const u32x4*>(xl + w_off(32 * xt + m, 8 * kp + 4 * kh + 2 * kq + q));
+                v8h wlo[2], whi[2];
+                // convert this chunk's W fragments before the next chunk is
+                // loaded into their registers
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    wlo[q] = cvt8(wreg[q].x, wreg[q].y);
+                    whi[q] = cvt8(wreg[q].z, wreg[q].w);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                {
+                    const int64_t cn = c + 1 < c1 ? c + 1 : c;   // last chunk: a harmless re-read
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        wreg[q] = __builtin_nontemporal_load(wsrc + cn * (8 * 2 * 64) + q * 64);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                v16f tmp[2];
+#pragma unroll
+                for (int xt = 0; xt < 2; ++xt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        tmp[xt][r] = 0.f;
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int xt = 0; xt < 2; ++xt) {
+                        const v8h xlo = cvt8(xv[xt][q].x, xv[xt][q].y), xhi = cvt8(xv[xt][q].z, xv[xt][q].w);
+                        tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wlo[q], xlo, tmp[xt], 0, 0, 0);
+                        tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(whi[q], xhi, tmp[xt], 0, 0, 0);
+                    }
 #pragma unroll
                 for (int xt = 0; xt < 2; ++xt) {
-                    const v8h xlo = cvt8(xv[xt][q].x, xv[xt][q].y), xhi = cvt8(xv[xt][q].z, xv[xt][q].w);
-                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wlo[q], xlo, tmp[xt], 0, 0, 0);
-                    tmp[xt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(whi[q], xhi, tmp[xt], 0, 0, 0);
+                    const float sc = lds_ps[(32 * xt + m) * GP + c * CH + kp];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[xt][r] = fmaf(tmp[xt][r], sc, acc[xt][r]);
                 }
-#pragma unroll
-            for (int xt = 0; xt < 2; ++xt) {
-                const float sc = lds_ps[(32 * xt + m) * GP + c * CH + kp];
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[xt][r] = fmaf(tmp[xt][r], sc, acc[xt][r]);
+                __syncthreads();                       // chunk drained, the next one landed
             }
-            __syncthreads();                       // chunk drained, the next one landed
         }
         __syncthreads();                           // the loader drained: the X ring is idle
         // the four (kp, kq) partials in the fixed order of decode_reduce_store,
@@ -1455,7 +1519,9 @@ void launch_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx, const uin
     const int64_t nch = K / (dec::CH * kGroup);
     const int64_t per = (nch + S - 1) / S;
     const dim3 grid((unsigned)(N / 64), (unsigned)S);
-    if (K / kGroup <= 64)
+    if (per == 14 && nch == S * per)               // the 8B down projection (K = 14336, 4 splits)
+        gemm_fwd_decode_packed_splitk_kernel<128, 14><<<grid, 576, 0, st>>>(p, ws, per);
+    else if (K / kGroup <= 64)
         gemm_fwd_decode_packed_splitk_kernel<64><<<grid, 576, 0, st>>>(p, ws, per);
     else
         gemm_fwd_decode_packed_splitk_kernel<128><<<grid, 576, 0, st>>>(p, ws, per);
