@@ -22,7 +22,8 @@ __all__ = [
     "lib", "Fp8LinError", "GROUP",
     "fp8_quant_act", "fp8_quant_weight", "fp8_weight_transpose", "fp8_weight_pack", "fp8_quant_transpose",
     "fp8_gemm_fwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed",
-    "fp8_gemm_fwd_packed_splitk", "fp8_gemm_fwd_packed_splitk_workspace", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
+    "fp8_gemm_fwd_packed_splitk", "fp8_gemm_fwd_packed_splitk_workspace", "fp8_gemm_fwd_packed_splitk_noalloc",
+    "SPLITK_SCRATCH_BYTES", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
     "fp8_rmsnorm_quant", "fp8_rmsnorm_bwd", "fp8_rmsnorm_bwd_workspace", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_swiglu_bwd_quant", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8_mxfp4_quant_weight", "fp8_gemm_fwd_w4",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
@@ -30,6 +31,7 @@ __all__ = [
 ]
 
 GROUP = 128
+SPLITK_SCRATCH_BYTES = 4 << 20     # FP8LIN_SPLITK_SCRATCH_BYTES
 SRC_BF16 = 0
 SRC_FP8_ROWQ = 1
 
@@ -57,6 +59,8 @@ _SYMBOLS = {
     "fp8_gemm_fwd_packed_splitk": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2 +
                                    [ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
     "fp8_gemm_fwd_packed_splitk_workspace": ([ctypes.c_int64] * 3, ctypes.c_int64),
+    "fp8_gemm_fwd_packed_splitk_noalloc": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2,
+                                           ctypes.c_int),
     "fp8_gemm_fwd_unified": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
     "fp8_linear_fwd": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 4, ctypes.c_int),
     "fp8_gemm_dgrad": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2, ctypes.c_int),
@@ -310,6 +314,24 @@ def fp8_gemm_fwd_packed_splitk(xq, sx, wqp, sw, workspace=None, out=None, stream
     _check(lib().fp8_gemm_fwd_packed_splitk(_ptr(xq), _ptr(sx), _ptr(wqp), _ptr(sw), M, N, K, _ptr(y),
                                             _ptr(workspace), workspace.numel() * 4, _stream(stream)),
            "fp8_gemm_fwd_packed_splitk")
+    return y
+
+
+def fp8_gemm_fwd_packed_splitk_noalloc(xq, sx, wqp, sw, out=None, stream=None):
+    """fp8_gemm_fwd_packed_splitk with its fp32 partial sums in the library's
+    static per-GPU scratch (FP8LIN_SPLITK_SCRATCH_BYTES): the C call allocates
+    nothing.  Pass `out` to keep this wrapper allocation-free as well.  Calls
+    that overlap on one GPU race on the shared scratch."""
+    M, K = xq.shape
+    N = wqp.shape[0]
+    _expect(xq, "xq", torch.uint8, (M, K))
+    _expect(sx, "sx", torch.float32, (M, K // GROUP))
+    _expect(wqp, "wqp", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    y = out if out is not None else _empty((M, N), torch.bfloat16, xq)
+    _expect(y, "y", torch.bfloat16, (M, N))
+    _check(lib().fp8_gemm_fwd_packed_splitk_noalloc(_ptr(xq), _ptr(sx), _ptr(wqp), _ptr(sw), M, N, K, _ptr(y),
+                                                    _stream(stream)), "fp8_gemm_fwd_packed_splitk_noalloc")
     return y
 
 
@@ -643,3 +665,4 @@ def fp8lin_decode_e4m3(q: torch.Tensor, method: int = 0, out=None, stream=None):
     x = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _check(lib().fp8lin_decode_e4m3(_ptr(q), q.numel(), _ptr(x), method, _stream(stream)), "fp8lin_decode_e4m3")
     return x
+

@@ -12,6 +12,8 @@
 
 #include "fp8lin_launch.hpp"
 
+static_assert(fp8lin::kSplitkScratchBytes == FP8LIN_SPLITK_SCRATCH_BYTES, "scratch size");
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -152,6 +154,9 @@ const char* fp8lin_status_string(int status)
     case FP8LIN_ERR_DEVICE: return "FP8LIN_ERR_DEVICE: no HIP device, or the current device is not gfx950";
     case FP8LIN_ERR_HIP: return "FP8LIN_ERR_HIP: a HIP call or kernel launch failed";
     case FP8LIN_ERR_ARG: return "FP8LIN_ERR_ARG: invalid argument combination";
+    case FP8LIN_ERR_SCRATCH:
+        return "FP8LIN_ERR_SCRATCH: the shape needs more scratch than the library's static device buffer "
+               "holds (FP8LIN_SPLITK_SCRATCH_BYTES); use the entry point that takes a workspace";
     default: return "FP8LIN: unknown status";
     }
 }
@@ -475,6 +480,47 @@ fp8lin_status fp8_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx, con
         fp8lin::launch_fill_zero_bf16(y, M * N, as_stream(stream));
     else
         fp8lin::launch_gemm_fwd_packed_splitk(xq, sx, wqp, sw, M, N, K, y, workspace, as_stream(stream));
+    return end_launch();
+}
+
+fp8lin_status fp8_gemm_fwd_packed_splitk_noalloc(const uint8_t* xq, const float* sx, const uint8_t* wqp,
+                                                 const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                                 void* stream)
+{
+    const int64_t need = fp8_gemm_fwd_packed_splitk_workspace(M, N, K);
+    if (need < 0)
+        return FP8LIN_ERR_SHAPE;
+    if (need > FP8LIN_SPLITK_SCRATCH_BYTES)
+        return FP8LIN_ERR_SCRATCH;
+    int64_t bx, bsx, bw, bsw, by;
+    if (!bytes_of(M, K, 1, &bx) || !bytes_of(M, K / kGroup, 4, &bsx) || !bytes_of(N, K, 1, &bw) ||
+        !bytes_of(N / kGroup, K / kGroup, 4, &bsw) || !bytes_of(M, N, 2, &by))
+        return FP8LIN_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        bx = bsx = bw = bsw = 0;
+    const Buf in[] = {{xq, bx}, {sx, bsx}, {wqp, bw}, {sw, bsw}};
+    const Buf out[] = {{y, by}};
+    fp8lin_status s = check_buffers(in, 4, out, 1);
+    if (s != FP8LIN_OK)
+        return s;
+    if (by == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = fp8lin::splitk_scratch(&ws);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            g_last_hip_error = (int)e;
+            return FP8LIN_ERR_HIP;
+        }
+    }
+    if (K == 0)
+        fp8lin::launch_fill_zero_bf16(y, M * N, as_stream(stream));
+    else
+        fp8lin::launch_gemm_fwd_packed_splitk(xq, sx, wqp, sw, M, N, K, y, static_cast<float*>(ws),
+                                              as_stream(stream));
     return end_launch();
 }
 

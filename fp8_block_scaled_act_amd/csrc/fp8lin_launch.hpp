@@ -47,6 +47,11 @@ void launch_gemm_fwd_packed(const uint8_t* xq, const float* sx, const uint8_t* w
 int64_t splitk_splits(int64_t N, int64_t K);
 void launch_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx, const uint8_t* wqp, const float* sw,
                                    int64_t M, int64_t N, int64_t K, void* y, float* ws, hipStream_t st);
+// Size of the per-GPU device array behind the allocation-free split-K entry
+// point, and its device address on the current device (looked up once per
+// device).
+constexpr int64_t kSplitkScratchBytes = int64_t(4) << 20;
+hipError_t splitk_scratch(void** out);
 void launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
                        int64_t T, int64_t N, int64_t K, void* dx, hipStream_t st);
 void launch_gemm_wgrad(const uint8_t* dyTq, const float* sdyT, const uint8_t* xTq, const float* sxT,

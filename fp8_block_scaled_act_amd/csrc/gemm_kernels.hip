@@ -53,6 +53,9 @@
 #include "fp8lin_device.hpp"
 #include "fp8lin_launch.hpp"
 
+#include <atomic>
+#include <mutex>
+
 namespace fp8lin {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -1528,6 +1531,50 @@ void launch_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx, const uin
     const int64_t mn = M * N;
     splitk_reduce_kernel<<<(unsigned)((mn / 4 + 255) / 256), 256, 0, st>>>(ws, (int)S, mn,
                                                                           static_cast<uint16_t*>(y));
+}
+
+// ------------------------------------------- allocation-free split-K scratch
+//
+// The fp32 partial sums [S][M][N] of the split-K decode GEMM for callers that
+// cannot allocate: a file-scope device array, one copy per GPU, alive until
+// the process ends and shared by every call on that GPU (calls that overlap
+// on one GPU race on it).  Every element a call reads was written by the same
+// call's split kernel, so nothing needs clearing.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// it looks up the device address once per device with hipGetSymbolAddress
+// and uses that pointer.
+static __device__ __align__(256) float scratch[kSplitkScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t splitk_scratch(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kScratchDevices)
+        return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            // the current device is `dev`: the address is that GPU's copy
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            if (p == nullptr)
+                return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 void launch_pack_decode(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wqp, hipStream_t st)

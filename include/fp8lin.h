@@ -67,8 +67,10 @@ typedef enum fp8lin_status {
     FP8LIN_ERR_ALIAS = 4,  /* an output overlaps an input or another output      */
     FP8LIN_ERR_DEVICE = 5, /* no HIP device, or the current device is not gfx950 */
     FP8LIN_ERR_HIP = 6,    /* a HIP call or kernel launch failed                 */
-    FP8LIN_ERR_ARG = 7     /* an enum argument is out of range, or an option is
+    FP8LIN_ERR_ARG = 7,    /* an enum argument is out of range, or an option is
                               not available for the chosen source kind           */
+    FP8LIN_ERR_SCRATCH = 8 /* the shape needs more than the static device scratch
+                              of an allocation-free entry point holds            */
 } fp8lin_status;
 
 /* Source kinds of fp8_quant_transpose. */
@@ -385,6 +387,33 @@ fp8lin_status fp8_gemm_fwd_packed_splitk(const uint8_t* xq, const float* sx,
                                          const uint8_t* wqp, const float* sw,
                                          int64_t M, int64_t N, int64_t K, void* y,
                                          float* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fp8_gemm_fwd_packed_splitk without a workspace argument, for callers that
+ * cannot allocate device memory or hand one in: code under HIP graph capture,
+ * tight serving loops, and harnesses that forbid allocation.  It performs no
+ * allocation (no hipMalloc, hipFree or allocating library routine): the fp32
+ * partial sums live in a device array inside the library, one copy per GPU,
+ * FP8LIN_SPLITK_SCRATCH_BYTES long, held until the process ends.
+ *   Arguments, layouts, limits and results as fp8_gemm_fwd_packed_splitk
+ *   (bit-identical to it for the same inputs).
+ *   The caller still passes every input and the output y.
+ *   A shape whose split needs more than FP8LIN_SPLITK_SCRATCH_BYTES
+ *   (fp8_gemm_fwd_packed_splitk_workspace(M, N, K) above it) returns
+ *   FP8LIN_ERR_SCRATCH before anything is enqueued.  The 8B MLP down
+ *   projection at 64 tokens (M = 64, N = 4096, K = 14336: 4 MiB) fits.
+ *   All calls on one GPU share its array and each leaves its partial sums
+ *   there: calls that may overlap on one GPU (different streams, or several
+ *   host threads without ordering) race and must not be issued; calls on one
+ *   stream are ordered and safe.
+ *   The first call on a device looks up that device's array address
+ *   (hipGetSymbolAddress, no allocation); a failure there is FP8LIN_ERR_HIP.
+ */
+#define FP8LIN_SPLITK_SCRATCH_BYTES (4 << 20)
+fp8lin_status fp8_gemm_fwd_packed_splitk_noalloc(const uint8_t* xq, const float* sx,
+                                                 const uint8_t* wqp, const float* sw,
+                                                 int64_t M, int64_t N, int64_t K, void* y,
+                                                 void* stream);
 
 /*
  * Forward GEMM with rollout and training on one kernel: the same product as

@@ -15,7 +15,7 @@ import fp8_block_scaled_act_amd as fl
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8lin.h")
 
-OK, NULL, SHAPE, ALIGN, ALIAS, DEVICE, HIP, ARG = range(8)
+OK, NULL, SHAPE, ALIGN, ALIAS, DEVICE, HIP, ARG, SCRATCH = range(9)
 HAS_GPU = torch.cuda.is_available()
 
 
@@ -41,7 +41,8 @@ def test_exports_every_declared_symbol(L):
               "fp8_gemm_dgrad_t", "fp8_gemm_wgrad", "fp8_rmsnorm_quant", "fp8_swiglu_quant",
               "fp8_mlp_fwd", "fp8_swiglu_bwd", "fp8_gemm_fwd_unified", "fp8_gemm_fwd_packed_splitk",
               "fp8_gemm_fwd_packed_splitk_workspace", "fp8_swiglu_bwd_quant", "fp8_rmsnorm_bwd",
-              "fp8_rmsnorm_bwd_workspace", "fp8lin_status_string", "fp8lin_last_hip_error"]:
+              "fp8_rmsnorm_bwd_workspace", "fp8_gemm_fwd_packed_splitk_noalloc", "fp8lin_status_string",
+              "fp8lin_last_hip_error"]:
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -49,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
+    for s in range(9):
         t = L.fp8lin_status_string(s).decode()
         assert t.startswith("FP8LIN_")
     assert "unknown" in L.fp8lin_status_string(99).decode()
@@ -231,6 +232,30 @@ def test_splitk_validation(L):
     assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 4096, 4096, E, F + 4, need, s0) == ALIGN
     assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 14336, 4096, E, None, 0, s0) == DEVICE    # no split
     assert L.fp8_gemm_fwd_packed_splitk(A, B, C, D, 64, 4096, 4096, E, F, need, s0) == DEVICE
+
+
+def test_splitk_noalloc_scratch_limit(L):
+    """The allocation-free split-K call holds its partial sums in a static
+    device array of FP8LIN_SPLITK_SCRATCH_BYTES; shapes that need more are
+    rejected on the host with FP8LIN_ERR_SCRATCH (checked before the device)."""
+    limit = fl.SPLITK_SCRATCH_BYTES
+    assert "FP8LIN_SPLITK_SCRATCH_BYTES (4 << 20)" in open(HEADER).read()
+    # the 8B down projection at 64 tokens needs exactly the whole array
+    assert L.fp8_gemm_fwd_packed_splitk_workspace(64, 4096, 14336) == limit
+    big = L.fp8_gemm_fwd_packed_splitk_workspace(64, 6144, 4096)
+    assert big > limit
+    assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D, 64, 6144, 4096, E, s0) == SCRATCH
+    assert "FP8LIN_ERR_SCRATCH" in L.fp8lin_status_string(SCRATCH).decode()
+    assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D, 65, 4096, 4096, E, s0) == SHAPE
+
+
+@fake_ptrs
+def test_splitk_noalloc_validation(L):
+    assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D, 64, 4096, 4096, C, s0) == ALIAS     # y over wqp
+    assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D + 4, 64, 4096, 4096, E, s0) == ALIGN
+    assert L.fp8_gemm_fwd_packed_splitk_noalloc(None, B, C, D, 64, 4096, 4096, E, s0) == NULL
+    assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D, 0, 4096, 4096, E, s0) == OK          # nothing to do
+    assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D, 64, 4096, 14336, E, s0) == DEVICE
 
 
 @fake_ptrs
