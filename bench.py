@@ -5,13 +5,16 @@
 
 A step is one pass of the layer's hot path over one batch of synthetic
 inputs already resident in HBM:
-  decode   (default) 8B-shaped MLP up-proj rollout step: 1x128 quantization of
+  large    (default) 32B-shaped forward: 1x128 quantization of X [16384,5120],
+           128x128 quantization of W [27648,5120] and the block-scaled GEMM,
+           all three inside the timed step; the decode step's kernels below
+           are timed beside it (under "kernels_decode")
+  decode   8B-shaped MLP up-proj rollout step: 1x128 quantization of
            X [64,4096] + block-scaled GEMM against W [14336,4096] quantized
            128x128 (and put in the decode layout, fp8_weight_pack) beforehand,
            as rollout does between optimizer steps; 10 weight copies are
            rotated so the weights come from HBM, not MALL
   prefill  7B-shaped forward: quantize X [8192,3584] and W [18944,3584], GEMM
-  large    32B-shaped forward: quantize X [16384,5120] and W [27648,5120], GEMM
   backward 8B-shaped backward: dual transpose-quant of dY [8192,14336],
            transpose-requant of the saved FP8 X [8192,4096], DGrad (as the NT
            GEMM on the transposed FP8 weight, made once with the weight
@@ -22,8 +25,11 @@ between device synchronisations.  value = GEMM TFLOP/s of the whole step.
 
 Also reported, per kernel: the average launch duration from HIP events around
 graph replays of that kernel alone on the same stream, with its algorithmic
-bytes or flops; `roofline` for the dominant kernel; `cpu_baseline`: the CPU
-oracle timed on a bounded sample of the same workload on this host.
+bytes or flops and its fraction of the roofline (GEMMs against the dense FP8
+MFMA peak, the metric's unit; the fp16 fraction beside it, since the codes are
+multiplied on the fp16 matrix core); `roofline` for the dominant kernel;
+`cpu_baseline`: the CPU oracle timed per stage on a bounded sample of the
+same workload on this host, extrapolated to the full step.
 """
 from __future__ import annotations
 
@@ -352,7 +358,98 @@ def time_graph(torch, g, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def time_kernels(torch, st, reps):
+    """Per kernel of a step: graph replays of that kernel alone (R launches per
+    replay over the rotated buffers), HIP events on the replaying stream."""
+    R = st.rotate
+    kernels = {}
+    for name, fn, kind, units in st.kernels:
+        gk = capture(torch, [fn], R)
+        ms = time_graph(torch, gk, reps) / R
+        if kind == "hbm":
+            ach, unit, peak = units / (ms * 1e-3) / 1e9, "GB/s", HBM_PEAK_GBS
+        else:
+            ach, unit, peak = units / (ms * 1e-3) / 1e12, "TFLOP/s", FP8_PEAK_TFLOPS
+        kernels[name] = {"us": round(ms * 1e3, 2), "achieved": round(ach, 1), "unit": unit,
+                         "frac": round(ach / peak, 4), "algorithmic": units}
+        if kind == "mfma":
+            kernels[name]["frac_of_fp16_peak"] = round(ach / F16_PEAK_TFLOPS, 4)
+        log("[bench]  %-26s %9.2f us  %9.1f %s" % (name, ms * 1e3, ach, unit))
+        del gk
+    return kernels
+
+
 # ------------------------------------------------------------ cpu baseline
+
+def host_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"nproc": avail, "cpu_model": model}
+
+
+def timed(fn, min_seconds, max_reps=1000):
+    """Repeat fn until min_seconds have passed; seconds per repetition."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            return dt / reps, reps
+
+
+def cpu_baseline_forward_stages(name, synthetic, budget=12.0):
+    """The oracle per stage of the forward step (activation quantization,
+    weight quantization, GEMM), each on a bounded sample of the workload and
+    extrapolated linearly in rows to the full step."""
+    import oracle
+    wl = synthetic.WORKLOADS[name]
+    M, N, K = wl.M, wl.N, wl.K
+    ra = min(M, 1024)
+    rw = min(N, 1024)
+    rg = min(M, 16)
+    x = synthetic.activations(M, K, seed=0, n_out=wl.n_out)[:max(ra, rg)]
+    w = synthetic.weights(N, K, seed=0)
+    wq, sw = oracle.quant_weight(w)                # the GEMM's operand (outside the timing)
+    wpart = w[:rw]
+    xq, sx = oracle.quant_act(x[:rg])
+    t_act, n_act = timed(lambda: oracle.quant_act(x[:ra]), 0.15 * budget)
+    t_wq, n_wq = timed(lambda: oracle.quant_weight(wpart), 0.15 * budget)
+    t_gemm, n_gemm = timed(lambda: oracle.gemm_fwd(xq, sx, wq, sw), 0.7 * budget)
+    full_act = t_act * M / ra
+    full_wq = t_wq * N / rw
+    full_gemm = t_gemm * M / rg
+    total = full_act + full_wq + full_gemm
+    stages = {
+        "quant_act": {"sample": "%d of %d rows" % (ra, M), "reps": n_act, "ms_sample": round(t_act * 1e3, 3),
+                      "ms_full": round(full_act * 1e3, 1),
+                      "GB/s": round(act_quant_bytes(ra, K) / t_act / 1e9, 3)},
+        "quant_weight": {"sample": "%d of %d rows" % (rw, N), "reps": n_wq, "ms_sample": round(t_wq * 1e3, 3),
+                         "ms_full": round(full_wq * 1e3, 1),
+                         "GB/s": round(weight_quant_bytes(rw, K) / t_wq / 1e9, 3)},
+        "gemm_fwd": {"sample": "%d of %d rows x all %d columns, fp64" % (rg, M, N), "reps": n_gemm,
+                     "ms_sample": round(t_gemm * 1e3, 3), "ms_full": round(full_gemm * 1e3, 1),
+                     "GFLOP/s": round(2 * rg * N * K / t_gemm / 1e9, 2)},
+    }
+    info = host_info()
+    return {"value": 2 * M * N * K / total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "nproc": info["nproc"], "cpu_model": info["cpu_model"],
+            "sample": "each stage timed on a sample of the step's inputs (see stages) and extrapolated "
+                      "linearly in rows to the full step; value = the step's GEMM flop / the extrapolated "
+                      "step time (%.1f s)" % total,
+            "ms_per_step_extrapolated": round(total * 1e3, 1), "stages": stages,
+            "seconds": round(n_act * t_act + n_wq * t_wq + n_gemm * t_gemm, 2)}
+
 
 def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
     """The oracle, as it stands, on a bounded sample of the workload: the
@@ -360,6 +457,8 @@ def cpu_baseline(name, synthetic, min_seconds=10.0, max_reps=200):
     import numpy as np
     import oracle
     wl = synthetic.WORKLOADS[name]
+    if name in ("large", "prefill", "tiny"):
+        return cpu_baseline_forward_stages(name, synthetic)
     if wl.kind == "forward":
         M, N, K = wl.M, wl.N, wl.K
         rows = min(M, 64)
@@ -601,11 +700,13 @@ def ingest_pmc(name, fetch_csv, write_csv, torch, fl, synthetic):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode", choices=["decode", "w4_decode", "decode_unified", "prefill", "large", "backward", "tiny", "producers", "mlp",
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large", choices=["decode", "w4_decode", "decode_unified", "prefill", "large", "backward", "tiny", "producers", "mlp",
                              "mlp_decode", "mlp_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="large: skip timing the decode step's kernels beside it")
     ap.add_argument("--profile-eager", action="store_true",
                     help="run each kernel of the step eagerly (for rocprofv3 counter passes) and exit")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -631,6 +732,7 @@ def main():
     log("[bench] workload", args.workload, "- building inputs")
     st = build_step(args.workload, torch, fl, synthetic)
     R = st.rotate
+    st_config = st.config
     steps = -(-args.steps // R) * R
     warm = -(-args.warmup // R) * R
 
@@ -654,36 +756,35 @@ def main():
 
     log("[bench] step: %.2f us, %.1f %s" % (ms_per_step * 1e3, value, value_unit))
     log("[bench] per-kernel timing")
-    kernels = {}
     reps = max(4, min(200, steps // R))
-    for name, fn, kind, units in st.kernels:
-        gk = capture(torch, [fn], R)
-        ms = time_graph(torch, gk, reps) / R
-        if kind == "hbm":
-            ach, unit, peak = units / (ms * 1e-3) / 1e9, "GB/s", HBM_PEAK_GBS
-        else:
-            ach, unit, peak = units / (ms * 1e-3) / 1e12, "TFLOP/s", F16_PEAK_TFLOPS
-        kernels[name] = {"us": round(ms * 1e3, 2), "achieved": round(ach, 1), "unit": unit,
-                         "frac": round(ach / peak, 4), "algorithmic": units}
-        if kind == "mfma":
-            kernels[name]["frac_of_fp8_peak"] = round(ach / FP8_PEAK_TFLOPS, 4)
-        log("[bench]  %-26s %9.2f us  %9.1f %s" % (name, ms * 1e3, ach, unit))
-        del gk
+    kernels = time_kernels(torch, st, reps)
     dom = st.dominant or max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
     kind = [k for (n, _, k, _) in st.kernels if n == dom][0]
     roofline = {"kernel": dom, "bound": kind, "achieved": dk["achieved"],
-                "peak": HBM_PEAK_GBS if kind == "hbm" else F16_PEAK_TFLOPS, "unit": dk["unit"],
+                "peak": HBM_PEAK_GBS if kind == "hbm" else FP8_PEAK_TFLOPS, "unit": dk["unit"],
                 "frac": dk["frac"], "traffic": None,
                 "algorithmic_per_launch": dk["algorithmic"], "avg_launch_us": dk["us"]}
     if kind == "mfma":
-        roofline["peak_note"] = "fp16 MFMA peak: FP8 codes are multiplied exactly on the fp16 matrix core"
-        roofline["frac_of_fp8_peak"] = dk["frac_of_fp8_peak"]
+        roofline["peak_note"] = ("dense FP8 MFMA peak (the metric's unit); the FP8 codes are multiplied "
+                                 "exactly on the fp16 matrix core, whose dense peak is 2500 TFLOP/s")
+        roofline["frac_of_fp16_peak"] = dk["frac_of_fp16_peak"]
     traffic_file = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(traffic_file):
         rec = json.load(open(traffic_file)).get("%s/%s" % (args.workload, dom))
         if rec and rec.get("source_sha") == source_hash(*KERNEL_SOURCES[dom]):
             roofline["traffic"] = rec["bytes_per_launch"]
+
+    extra = {}
+    if args.workload == "large" and not args.no_extra:
+        # the decode step's kernels, timed the same way (its own rotated weights)
+        del st, g_step
+        torch.cuda.empty_cache()
+        log("[bench] decode step kernels (8B up-proj, X[64,4096], W[14336,4096])")
+        sd = build_step("decode", torch, fl, synthetic)
+        extra = {"workload": sd.config["workload"], "weight_copies_rotated": sd.rotate,
+                 "kernels": time_kernels(torch, sd, 200)}
+        del sd
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -697,8 +798,13 @@ def main():
         "value": round(value, 2), "unit": value_unit, "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
-        "config": st.config, "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "config": st_config, "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
+    if R > 1 and (steps != args.steps or warm != args.warmup):
+        line["rounding"] = ("steps and warmup rounded up to a multiple of the %d-copy weight rotation "
+                            "(asked: %d and %d)" % (R, args.steps, args.warmup))
+    if extra:
+        line["kernels_decode"] = extra
     print(json.dumps(line), flush=True)
 
 
