@@ -26,7 +26,7 @@ __all__ = [
     "SPLITK_SCRATCH_BYTES", "fp8_linear_fwd", "fp8_gemm_dgrad", "fp8_gemm_dgrad_t", "fp8_gemm_wgrad",
     "fp8_rmsnorm_quant", "fp8_rmsnorm_bwd", "fp8_rmsnorm_bwd_workspace", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_swiglu_bwd_quant", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8_mxfp4_quant_weight", "fp8_gemm_fwd_w4",
-    "fp8lin_encode_e4m3", "fp8lin_decode_e4m3",
+    "fp8lin_encode_e4m3", "fp8lin_decode_e4m3", "fp8lin_gemm_fwd_mfma_probe", "MFMA_PROBE_FORMS",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
 
@@ -86,6 +86,8 @@ _SYMBOLS = {
                            ctypes.c_int),
     "fp8lin_decode_e4m3": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
                            ctypes.c_int),
+    "fp8lin_gemm_fwd_mfma_probe": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 +
+                                   [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p], ctypes.c_int),
 }
 
 _lib = None
@@ -666,3 +668,27 @@ def fp8lin_decode_e4m3(q: torch.Tensor, method: int = 0, out=None, stream=None):
     _check(lib().fp8lin_decode_e4m3(_ptr(q), q.numel(), _ptr(x), method, _stream(stream)), "fp8lin_decode_e4m3")
     return x
 
+
+MFMA_PROBE_FORMS = {
+    0: "v_mfma_scale_f32_16x16x128_f8f6f4",
+    1: "v_mfma_scale_f32_32x32x64_f8f6f4",
+    2: "v_mfma_f32_16x16x32_fp8_fp8",
+    3: "v_mfma_f32_32x32x16_fp8_fp8",
+    4: "v_mfma_f32_32x32x16_f16 (control: codes converted exactly to fp16)",
+}
+
+
+def fp8lin_gemm_fwd_mfma_probe(xq, sx, wq, sw, form: int, out=None, stream=None):
+    """Diagnostic: fp8_gemm_fwd's product on matrix-core form `form` (see
+    MFMA_PROBE_FORMS), fp32 output [M,N]."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    _expect(xq, "xq", torch.uint8, (M, K))
+    _expect(sx, "sx", torch.float32, (M, K // GROUP))
+    _expect(wq, "wq", torch.uint8, (N, K))
+    _expect(sw, "sw", torch.float32, (N // GROUP, K // GROUP))
+    y = out if out is not None else _empty((M, N), torch.float32, xq)
+    _expect(y, "y", torch.float32, (M, N))
+    _check(lib().fp8lin_gemm_fwd_mfma_probe(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), int(form),
+                                            _stream(stream)), "fp8lin_gemm_fwd_mfma_probe")
+    return y

@@ -829,6 +829,30 @@ fp8lin_status fp8lin_encode_e4m3(const float* in, int64_t n, uint8_t* out, int m
     return end_launch();
 }
 
+fp8lin_status fp8lin_gemm_fwd_mfma_probe(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                         int64_t M, int64_t N, int64_t K, float* y, int form, void* stream)
+{
+    if (M < 0 || N < 0 || K <= 0 || N % kGroup != 0 || K % kGroup != 0 || M / 16 >= kMaxGridY)
+        return FP8LIN_ERR_SHAPE;
+    if (form < 0 || form > 4)
+        return FP8LIN_ERR_ARG;
+    int64_t bx, bsx, bw, bsw, by;
+    if (!bytes_of(M, K, 1, &bx) || !bytes_of(M, K / kGroup, 4, &bsx) || !bytes_of(N, K, 1, &bw) ||
+        !bytes_of(N / kGroup, K / kGroup, 4, &bsw) || !bytes_of(M, N, 4, &by))
+        return FP8LIN_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return FP8LIN_OK;
+    const Buf in[] = {{xq, bx}, {sx, bsx}, {wq, bw}, {sw, bsw}};
+    const Buf out[] = {{y, by}};
+    fp8lin_status s = check_buffers(in, 4, out, 1);
+    if (s != FP8LIN_OK)
+        return s;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_gemm_fwd_mfma_probe(xq, sx, wq, sw, M, N, K, y, form, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int method, void* stream)
 {
     if (n < 0)

@@ -15,6 +15,11 @@ void launch_quant_transpose_fp8(const uint8_t* src, const float* srow, int64_t T
                                 uint8_t* qT, float* sT, hipStream_t st);
 void launch_transpose_codes(const uint8_t* src, const float* s, int64_t R, int64_t C, uint8_t* dst, float* sT,
                             hipStream_t st);
+// Diagnostic: the block-scaled forward product on FP8 MFMA form `form` (0..3)
+// or the fp16 control (4), fp32 output [M][N]; N % 128 == 0, K % 128 == 0, M >= 1.
+int mfma_probe_tile(int form);
+void launch_gemm_fwd_mfma_probe(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                                int64_t N, int64_t K, float* y, int form, hipStream_t st);
 void launch_encode_probe(const float* in, int64_t n, uint8_t* out, int method, hipStream_t st);
 void launch_decode_probe(const uint8_t* in, int64_t n, float* out, int method, hipStream_t st);
 

@@ -530,6 +530,31 @@ fp8lin_status fp8_gemm_fwd_w4(const uint8_t* xq, const float* sx,
 fp8lin_status fp8lin_encode_e4m3(const float* in, int64_t n, uint8_t* out, int method, void* stream);
 fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int method, void* stream);
 
+/*
+ * Diagnostic: the forward product of fp8_gemm_fwd (Jet-RL summary,
+ * "Quantization scheme": FP8 codes, one scale per 128-wide contraction group
+ * from 1x128 activation and 128x128 weight quantization) computed by a plain
+ * one-wave-per-tile kernel on a chosen matrix-core instruction, written as
+ * fp32 sums, so that tests can record how accurate each instruction is:
+ *   form 0: v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 operands, unit scales)
+ *   form 1: v_mfma_scale_f32_32x32x64_f8f6f4
+ *   form 2: v_mfma_f32_16x16x32_fp8_fp8
+ *   form 3: v_mfma_f32_32x32x16_fp8_fp8
+ *   form 4: v_mfma_f32_32x32x16_f16 on the codes converted exactly to fp16
+ *           (the instruction of the library's GEMMs), as the control.
+ * Each 128-group's partial product is one chain of the form's instructions
+ * from zero, added into the fp32 sum times sx * sw with one fused
+ * multiply-add, groups in ascending order; only the instruction differs
+ * between forms.  Not tuned for speed.
+ *   xq, sx, wq, sw : as fp8_gemm_fwd;  y : float [M,N] (output)
+ * N % 128 == 0, K % 128 == 0, K > 0, M >= 0 (M/16 < 65535), else FP8LIN_ERR_SHAPE;
+ * form outside 0..4: FP8LIN_ERR_ARG.  M == 0 or N == 0 is an OK no-op.
+ */
+fp8lin_status fp8lin_gemm_fwd_mfma_probe(const uint8_t* xq, const float* sx,
+                                         const uint8_t* wq, const float* sw,
+                                         int64_t M, int64_t N, int64_t K,
+                                         float* y, int form, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

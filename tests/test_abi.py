@@ -250,6 +250,18 @@ def test_splitk_noalloc_scratch_limit(L):
 
 
 @fake_ptrs
+def test_mfma_probe_validation(L):
+    f = L.fp8lin_gemm_fwd_mfma_probe
+    assert f(A, B, C, D, 16, 256, 256, E, 5, s0) == ARG                # no such form
+    assert f(A, B, C, D, 16, 256, 256, E, -1, s0) == ARG
+    assert f(A, B, C, D, 16, 200, 256, E, 0, s0) == SHAPE              # N % 128
+    assert f(A, B, C, D, 16, 256, 0, E, 0, s0) == SHAPE                # K == 0
+    assert f(A, B, C, D, 0, 256, 256, E, 0, s0) == OK                  # nothing to do
+    assert f(A, B, C, D, 16, 256, 256, C, 0, s0) == ALIAS
+    assert f(A, B, C, D, 16, 256, 256, E, 0, s0) == DEVICE
+
+
+@fake_ptrs
 def test_splitk_noalloc_validation(L):
     assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D, 64, 4096, 4096, C, s0) == ALIAS     # y over wqp
     assert L.fp8_gemm_fwd_packed_splitk_noalloc(A, B, C, D + 4, 64, 4096, 4096, E, s0) == ALIGN
