@@ -149,6 +149,22 @@ def _expect(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) -> Non
         raise ValueError("%s must be on the GPU" % name)
 
 
+def _expect_workspace(ws: torch.Tensor, name: str, dtype: torch.dtype, like: torch.Tensor) -> int:
+    """Checks a caller workspace like any other operand (a tensor of `dtype`,
+    contiguous, on the device of `like`) and returns its size in bytes."""
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if ws.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, ws.dtype))
+    if not ws.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if not ws.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if like.is_cuda and ws.device != like.device:
+        raise ValueError("%s must be on %s, got %s" % (name, like.device, ws.device))
+    return ws.numel() * ws.element_size()
+
+
 def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
     return torch.empty(shape, dtype=dtype, device=like.device)
 
@@ -309,12 +325,11 @@ def fp8_gemm_fwd_packed_splitk(xq, sx, wqp, sw, workspace=None, out=None, stream
     need = fp8_gemm_fwd_packed_splitk_workspace(M, N, K)
     if workspace is None:
         workspace = _empty((max(need // 4, 1),), torch.float32, xq)
-    if workspace.dtype != torch.float32 or not workspace.is_contiguous():
-        raise TypeError("workspace must be a contiguous float32 tensor")
+    nbytes = _expect_workspace(workspace, "workspace", torch.float32, xq)
     y = out if out is not None else _empty((M, N), torch.bfloat16, xq)
     _expect(y, "y", torch.bfloat16, (M, N))
     _check(lib().fp8_gemm_fwd_packed_splitk(_ptr(xq), _ptr(sx), _ptr(wqp), _ptr(sw), M, N, K, _ptr(y),
-                                            _ptr(workspace), workspace.numel() * 4, _stream(stream)),
+                                            _ptr(workspace), nbytes, _stream(stream)),
            "fp8_gemm_fwd_packed_splitk")
     return y
 
@@ -440,7 +455,7 @@ def fp8_rmsnorm_bwd(x, gamma, rstd, dy, dgamma: bool = True, workspace=None, out
     need = fp8_rmsnorm_bwd_workspace(M, K) if dg is not None else 0
     if workspace is None and need:
         workspace = _empty((need // 8,), torch.float64, x)
-    nbytes = workspace.numel() * 8 if workspace is not None else 0
+    nbytes = _expect_workspace(workspace, "workspace", torch.float64, x) if workspace is not None else 0
     _check(lib().fp8_rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(rstd), _ptr(dy), M, K, _ptr(dx), _ptr(dg),
                                  _ptr(workspace), nbytes, _stream(stream)), "fp8_rmsnorm_bwd")
     return dx, dg

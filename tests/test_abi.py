@@ -391,3 +391,24 @@ def test_gemm_fwd_w4_validation(L):
     assert L.fp8_gemm_fwd_w4(A, B, C, D, 4, 100, 128, C, s0) == ALIAS
     assert L.fp8_gemm_fwd_w4(None, None, None, None, 0, 100, 128, None, s0) == OK
     assert L.fp8_gemm_fwd_w4(A, B, C, D, 4, 100, 128, E, s0) == DEVICE    # any N
+
+
+def test_binding_rejects_bad_workspaces():
+    """Caller workspaces are checked like any other operand before the C call:
+    wrong dtype -> TypeError, host memory or a non-contiguous view ->
+    ValueError (zero-sized operands, so no device memory is needed here)."""
+    bf, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+    x = torch.empty((0, 0), dtype=bf)
+    args = (x, torch.empty((0,), dtype=bf), torch.empty((0,), dtype=f32), torch.empty((0, 0), dtype=bf))
+    with pytest.raises(TypeError, match="workspace must be torch.float64"):
+        fl.fp8_rmsnorm_bwd(*args, workspace=torch.empty((16,), dtype=f32))
+    with pytest.raises(ValueError, match="workspace must be on the GPU"):
+        fl.fp8_rmsnorm_bwd(*args, workspace=torch.empty((16,), dtype=torch.float64))
+    with pytest.raises(ValueError, match="workspace must be contiguous"):
+        fl.fp8_rmsnorm_bwd(*args, workspace=torch.empty((16, 2), dtype=torch.float64)[:, 0])
+    g = (torch.empty((0, 0), dtype=u8), torch.empty((0, 0), dtype=f32), torch.empty((128, 0), dtype=u8),
+         torch.empty((1, 0), dtype=f32))
+    with pytest.raises(TypeError, match="workspace must be torch.float32"):
+        fl.fp8_gemm_fwd_packed_splitk(*g, workspace=torch.empty((16,), dtype=torch.float64))
+    with pytest.raises(ValueError, match="workspace must be on the GPU"):
+        fl.fp8_gemm_fwd_packed_splitk(*g, workspace=torch.empty((16,), dtype=f32))
