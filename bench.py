@@ -626,6 +626,11 @@ KERNEL_SYMBOLS = {           # bench kernel name -> substring of the HIP symbol
 }
 
 
+# (workload, kernel) pairs whose HIP kernel also runs at another shape in the
+# same step under another name: their counters cannot be told apart
+AMBIGUOUS_SYMBOLS = {("mlp_train", "quant_transpose_fp8_X")}   # also the H requant
+
+
 def profile_eager(name, torch, fl, synthetic):
     st = build_step(name, torch, fl, synthetic)
     src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -674,7 +679,7 @@ def ingest_pmc(name, fetch_csv, write_csv, torch, fl, synthetic):
     data = json.load(open(path)) if os.path.exists(path) else {}
     for kname, _, kind, units in st.kernels:
         sym = KERNEL_SYMBOLS[kname]
-        if sym is None:
+        if sym is None or (name, kname) in AMBIGUOUS_SYMBOLS:
             continue
         pred = lambda k, sym=sym: sym in k and not copy_pred(k)
         f, w = avg_kib(fetch, pred), avg_kib(write, pred)

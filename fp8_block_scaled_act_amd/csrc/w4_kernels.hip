@@ -1,9 +1,10 @@
 // w4_kernels.hip -- 4-bit (MXFP4) weights for the rollout GEMM, gfx950.
 //
-// QeRL (arXiv 2510.11696, abstract) runs the rollout on 4-bit NVFP4 weights
-// and gives no format details.  NVFP4 belongs to NVIDIA's Blackwell; gfx950's
-// converters and matrix cores take the OCP Microscaling formats, so the
-// weights here are MXFP4 as OCP MX v1.0 defines it:
+// The QeRL page ("QeRL: Beyond Efficiency -- Quantization-enhanced
+// Reinforcement Learning for LLMs", abstract) runs the rollout on 4-bit NVFP4
+// weights and gives no format details.  NVFP4 belongs to NVIDIA's Blackwell;
+// gfx950's converters and matrix cores take the OCP Microscaling formats, so
+// the weights here are MXFP4 as OCP MX v1.0 defines it:
 //   - E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit;
 //     magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6);
 //   - 32 consecutive elements of a weight row share one E8M0 scale 2^E,

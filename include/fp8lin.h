@@ -479,9 +479,10 @@ fp8lin_status fp8_gemm_wgrad(const uint8_t* dyTq, const float* sdyT,
 
 /*
  * 4-bit weights for the rollout GEMM: MXFP4 quantization of BF16 weights
- * (once per optimizer step).  QeRL (arXiv 2510.11696, abstract) runs the
- * rollout on 4-bit NVFP4 weights without giving the format; it is read here
- * as OCP MX v1.0 MXFP4, the 4-bit format gfx950 converts natively:
+ * (once per optimizer step).  The QeRL page ("QeRL: Beyond Efficiency --
+ * Quantization-enhanced Reinforcement Learning for LLMs", abstract) runs the
+ * rollout on 4-bit NVFP4 weights without giving the format; it is read here as
+ * OCP MX v1.0 MXFP4, the 4-bit format gfx950 converts natively:
  *   w      : BF16 [N,K]                (input)
  *   codes  : uint8 [N][K/2]            (output) E2M1 codes, two per byte, the
  *            even k in the low nibble (sign bit 3, exponent bits 2..1 with
@@ -499,7 +500,8 @@ fp8lin_status fp8_mxfp4_quant_weight(const void* w, int64_t N, int64_t K,
 /*
  * Rollout GEMM on 4-bit weights (NT):  Y = X W^T, with the activations in the
  * flow's FP8 1x128 groups (fp8_quant_act) and W from fp8_mxfp4_quant_weight.
- * QeRL (arXiv 2510.11696, abstract): 4-bit weights for the rollout.
+ * The QeRL page ("QeRL: Beyond Efficiency -- Quantization-enhanced
+ * Reinforcement Learning for LLMs", abstract): 4-bit weights for the rollout.
  *   Y[m,n] = sum_g sx[m][g] * sum_{k in g} dec(xq[m,k]) * e2m1(w[n,k]) * 2^E[n][k/32]
  *   xq : [M,K], sx : [M][K/128], codes : [N][K/2], scales : [N][K/32]
  *   y  : BF16 [M,N] (output), fp32 accumulation, round-to-nearest-even.

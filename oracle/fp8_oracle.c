@@ -501,8 +501,9 @@ void oracle_swiglu_bwd_bf16(const uint16_t* g, const uint16_t* u, const uint16_t
 
 /* ------------------------------------------------ 4-bit weights (MXFP4)
  *
- * QeRL (arXiv 2510.11696, abstract) speeds up the rollout with 4-bit NVFP4
- * weights plus LoRA; the page gives no format details.  NVFP4 belongs to
+ * The QeRL page ("QeRL: Beyond Efficiency -- Quantization-enhanced
+ * Reinforcement Learning for LLMs", abstract) speeds up the rollout with 4-bit
+ * NVFP4 weights plus LoRA; the page gives no format details.  NVFP4 belongs to
  * NVIDIA's Blackwell; the MI355X converters and matrix cores take the OCP
  * Microscaling (MX) formats, so the 4-bit weights here are MXFP4 as the OCP
  * MX specification v1.0 defines it (the project's reading):

@@ -1,7 +1,8 @@
 """Pins of the oracle's 4-bit MXFP4 weight format and the GEMM on it.
 
-QeRL (arXiv 2510.11696, abstract) gives its rollout weights as 4-bit NVFP4
-and no format details; the oracle reads them as OCP MXFP4 (E2M1 elements, 32
+The QeRL page ("QeRL: Beyond Efficiency -- Quantization-enhanced Reinforcement
+Learning for LLMs", abstract) gives its rollout weights as 4-bit NVFP4 and no
+format details; the oracle reads them as OCP MXFP4 (E2M1 elements, 32
 per block along K, one E8M0 power-of-two scale per block, scale exponent
 floor(log2(amax)) - 2, round to nearest with ties to even, saturation at 6).
 Each test checks the oracle against something other than itself: the value
