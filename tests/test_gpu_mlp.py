@@ -1,14 +1,15 @@
 """GPU tests of the forward FP8 MLP block (fp8_mlp_fwd): RMSNorm -> gate/up
 GEMM -> SwiGLU -> down GEMM in one call.
 
-Each stage must be bit-identical to the separate entry point (those are
-parity-tested against the oracle on their own); the FP8 input of the first
-GEMM is bit-exact against the oracle; the gate/up output meets the GEMM
-metric; and the block's output is compared end to end with the oracle chain
-(oracle quantizers, fp64 GEMMs, bf16 rounding of the gate/up output as the
-block stores it).  End to end, the two chains round the gate/up product
-separately (fp32 vs fp64 accumulation), which can move a SwiGLU code by one
-step; the tolerance is therefore on the rms-relative error, 1e-2."""
+Each stage must be bit-identical to the separate entry point, and each is
+checked against the oracle on its own GPU inputs: the FP8 input of the first
+GEMM bit-exact, the gate/up output within the GEMM metric, the SwiGLU
+quantization bit-exact on the GPU's gate/up output (valid roundings at
+near-ties), the down projection within the metric on the GPU's FP8 H.  The
+block's output is also compared end to end with the all-oracle chain; there
+the two chains round the gate/up product separately (fp32 vs fp64
+accumulation), which can move a SwiGLU code by one step, so that comparison is
+on the rms-relative error, 1e-2."""
 import numpy as np
 import pytest
 import torch
@@ -17,6 +18,7 @@ import fp8_block_scaled_act_amd as fl
 import oracle
 import synthetic
 from gpu_util import DEV, bf16_bits_to_f64, bf16_to_dev, f32_to_dev, first_mismatch, host, say, u8_to_dev
+from near_tie import check_rowq_near_ties
 
 pytestmark = pytest.mark.gpu
 G = 128
@@ -71,6 +73,14 @@ def run_block(T, K, F, seed, rows=None, eps=1e-6):
     ref_gu = oracle.gemm_fwd(oxq, osx, owgu, osgu)
     err_gu = oracle.gemm_metric(bf16_bits_to_f64(host(out["gu"])[sel]), ref_gu)
     assert err_gu <= TOL, err_gu
+    # each later stage on its GPU inputs: SwiGLU quantization on the GPU's gu
+    # (bit for bit, valid roundings at near-ties), the down GEMM on the GPU's hq
+    gu_g = host(out["gu"])[sel]
+    h, near = oracle.swiglu_bf16(np.ascontiguousarray(gu_g[:, :F]), np.ascontiguousarray(gu_g[:, F:]))
+    check_rowq_near_ties(h, near, host(out["hq"])[sel], host(out["sh"])[sel], "SwiGLU quantization")
+    err_y = oracle.gemm_metric(bf16_bits_to_f64(host(out["y"])[sel]),
+                               oracle.gemm_fwd(host(out["hq"])[sel], host(out["sh"])[sel], owd, osd))
+    assert err_y <= TOL, err_y
     yg = bf16_bits_to_f64(host(out["y"])[sel])
     rel = float(np.sqrt(np.mean((yg - oy) ** 2)) / np.sqrt(np.mean(oy * oy)))
     gu_same = float(np.mean(host(out["gu"])[sel] == ogu))
