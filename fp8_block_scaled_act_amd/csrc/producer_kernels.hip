@@ -328,15 +328,27 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_dgamma_partial_kernel(const u
     ws[(int64_t)blockIdx.y * K + col + 1] = a1;
 }
 
-__global__ __launch_bounds__(256) void rmsnorm_bwd_dgamma_final_kernel(const double* __restrict__ ws,
-                                                                       int64_t nblocks, int64_t K,
-                                                                       float* __restrict__ dgamma)
+// dgamma[k] = fp32 of the block partials added in ascending block order; 32
+// blocks' loads in flight per thread.
+__global__ __launch_bounds__(64) void rmsnorm_bwd_dgamma_final_kernel(const double* __restrict__ ws,
+                                                                      int64_t nblocks, int64_t K,
+                                                                      float* __restrict__ dgamma)
 {
-    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t k = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (k >= K)
         return;
     double total = 0.0;
-    for (int64_t b = 0; b < nblocks; ++b)
+    int64_t b = 0;
+    for (; b + 32 <= nblocks; b += 32) {
+        double v[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+            v[u] = ws[(b + u) * K + k];
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+            total = total + v[u];
+    }
+    for (; b < nblocks; ++b)
         total = total + ws[b * K + k];
     dgamma[k] = (float)total;
 }
@@ -712,7 +724,7 @@ void launch_rmsnorm_bwd(const void* x, const void* gamma, const float* rstd, con
         const int64_t nb = (M + kGroup - 1) / kGroup;
         const dim3 grid((unsigned)((K + 511) / 512), (unsigned)nb);
         rmsnorm_bwd_dgamma_partial_kernel<<<grid, 256, 0, st>>>(xp, rstd, dp, M, K, ws);
-        rmsnorm_bwd_dgamma_final_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(ws, nb, K, dgamma);
+        rmsnorm_bwd_dgamma_final_kernel<<<(unsigned)((K + 63) / 64), 64, 0, st>>>(ws, nb, K, dgamma);
     }
 }
 
