@@ -27,6 +27,7 @@ __all__ = [
     "fp8_rmsnorm_quant", "fp8_rmsnorm_bwd", "fp8_rmsnorm_bwd_workspace", "fp8_swiglu_quant", "fp8_swiglu_bwd", "fp8_swiglu_bwd_quant", "fp8_mlp_fwd", "fp8_mlp_bwd",
     "fp8_mxfp4_quant_weight", "fp8_gemm_fwd_w4",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3", "fp8lin_gemm_fwd_mfma_probe", "MFMA_PROBE_FORMS",
+    "fp8lin_math_probe",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
 
@@ -88,6 +89,8 @@ _SYMBOLS = {
                            ctypes.c_int),
     "fp8lin_gemm_fwd_mfma_probe": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 +
                                    [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p], ctypes.c_int),
+    "fp8lin_math_probe": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
+                          ctypes.c_int),
 }
 
 _lib = None
@@ -682,6 +685,16 @@ def fp8lin_decode_e4m3(q: torch.Tensor, method: int = 0, out=None, stream=None):
     x = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _check(lib().fp8lin_decode_e4m3(_ptr(q), q.numel(), _ptr(x), method, _stream(stream)), "fp8lin_decode_e4m3")
     return x
+
+
+def fp8lin_math_probe(x: torch.Tensor, fn: int, out=None, stream=None):
+    """Device fp32 hardware function on a flat float32 tensor: fn 0 = 2^x
+    (v_exp_f32), fn 1 = 1/x (v_rcp_f32)."""
+    _expect(x, "in", torch.float32, tuple(x.shape))
+    y = out if out is not None else torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _expect(y, "out", torch.float32, tuple(x.shape))
+    _check(lib().fp8lin_math_probe(_ptr(x), x.numel(), _ptr(y), int(fn), _stream(stream)), "fp8lin_math_probe")
+    return y
 
 
 MFMA_PROBE_FORMS = {

@@ -359,14 +359,15 @@ __global__ __launch_bounds__(64) void rmsnorm_bwd_dgamma_final_kernel(const doub
 // BF16; its error (a few fp64 ulps) cannot move the rounding except within
 // 2^-44 of a BF16 midpoint.  The kernel first evaluates in fp32:
 //   e = v_exp_f32(g * fl(-log2 e)),  v = (g * v_rcp_f32(1 + e)) * u.
-// For |g| < 64 its relative error is at most
-//   |g| 2^-23 (the rounded exponent argument, times ln 2)
-//   + 2 ulp (exp) + 1 ulp (rcp) + 2 half-ulp roundings (add, products)
-//   <= 137 * 2^-24, i.e. at most ~140 ulps of v;
-// so when v's fp32 bits lie more than 512 ulps from a BF16 midpoint (low 16
-// bits outside [0x7E00, 0x8200]) the exact value rounds to the same BF16 as v.
-// Every other element, and every |g| >= 64, is evaluated again in fp64 (about
-// 1.6% of elements; the wave loops over each lane's flagged elements).
+// For |g| < 64 its relative error is at most (eps = 2^-24)
+//   2|g| eps (the rounded exponent argument, times ln 2)
+//   + 4 eps (exp, within 2 ulp) + 2 eps (rcp, within 1 ulp)
+//   + 3 eps (the add and the two products)  <=  (2|g| + 9) eps,
+// the two hardware bounds measured on every argument these kernels pass.
+// Elements whose fp32 value may round differently from the exact one
+// (needs_f64 with B = 2|g| + 10 ulps) and every |g| >= 64 are evaluated
+// again in fp64, one flagged element at a time per lane; an exact zero
+// (g = 0 or u = 0: a signed zero on both routes) never is.
 __device__ __forceinline__ uint32_t swiglu_bf16_f64(float g, float u)
 {
     const double gd = g, ud = u;
@@ -375,12 +376,29 @@ __device__ __forceinline__ uint32_t swiglu_bf16_f64(float g, float u)
 
 // The fp32 value (rounded to BF16 by the caller) and whether it must be
 // evaluated again in fp64.
+// True when the fp32 value v, within `ulps` ulps of the exact value, may
+// round to a different BF16 than the exact value (a BF16 rounding midpoint
+// lies within ulps + 2 ulps of v; the 2 cover the second-order terms the
+// bounds leave out), or when v lies outside [2^-100, 2^101), where an
+// intermediate could under- or overflow and the relative bounds do not hold.
+// A relative error of B eps (eps = 2^-24) is at most B ulps of the result.
+__device__ __forceinline__ bool needs_f64(float v, float ulps)
+{
+    // for 0 <= lim <= 2^15: |low 16 bits - 0x8000| <= lim  <=>
+    // (low - 0x8000 + lim) mod 2^16 <= 2 lim (lim = 2^15 flags every value)
+    const uint32_t lim = (uint32_t)__builtin_amdgcn_fmed3f(ulps + 2.0f, 0.0f, 32768.0f);
+    const uint32_t t = (__float_as_uint(v) + lim - 0x8000u) & 0xFFFFu;
+    const float a = __builtin_fabsf(v);
+    return t <= 2u * lim || !(a >= 0x1p-100f && a < 0x1p101f);
+}
+
 __device__ __forceinline__ float swiglu_f32(float g, float u, bool& redo)
 {
     const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
     const float v = (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
-    const uint32_t b = __float_as_uint(v);
-    redo = ((b - 0x7E00u) & 0xFFFFu) <= 0x400u || __builtin_fabsf(g) >= 64.0f;
+    const float ag = __builtin_fabsf(g);
+    const bool exact_zero = g == 0.0f || u == 0.0f;
+    redo = !exact_zero && (ag >= 64.0f || needs_f64(v, 2.0f * ag + 10.0f));
     return v;
 }
 
@@ -474,30 +492,19 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
 //   q = g t,  w = 1 + q                 w: <= (|q| / |w|) (4|g| + 13) eps + eps
 //   d_up   = (dh g) s                   <= (2|g| + 8) eps
 //   d_gate = ((dh u) s) w               <= (2|g| + 10 + (|q| / |w|)(4|g| + 13)) eps
-// A relative error of B eps is at most B ulps of the fp32 result, so an
-// output whose fp32 bits lie more than 2B + 2 ulps from a BF16 midpoint
-// rounds as the exact value does.  The others, |g| >= 64 (exponent argument
-// error and exp range), results outside [2^-100, 2^101) (where an
-// intermediate could under- or overflow) and w = 0 are evaluated again in
-// fp64, one flagged element at a time per lane.
+// (exp within 2 ulp and rcp within 1 ulp, measured on every argument these
+// kernels pass).  A relative error of B eps is at most B ulps of the fp32
+// result, so an output whose fp32 bits lie more than B + 2 ulps from a BF16
+// midpoint rounds as the exact value does (needs_f64).  The others, |g| >= 64
+// (exponent argument error and exp range), results outside [2^-100, 2^101)
+// (where an intermediate could under- or overflow) and w = 0 are evaluated
+// again in fp64, one flagged element at a time per lane.
 __device__ __forceinline__ void swiglu_bwd_f64(float gf, float uf, float df, uint32_t& bg, uint32_t& bu)
 {
     const double g = gf, u = uf, d = df;
     const double sg = 1.0 / (1.0 + exp(-g));
     bg = f64_to_bf16_rne(((d * u) * sg) * (1.0 + g * (1.0 - sg)));
     bu = f64_to_bf16_rne(d * (g * sg));
-}
-
-// true when fp32 v may round to a different BF16 than a value within `ulps`
-// ulps of it, or lies outside the range where the bound holds
-__device__ __forceinline__ bool needs_f64(float v, float ulps)
-{
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t low = b & 0xFFFFu;
-    const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
-    const uint32_t ex = (b >> 23) & 0xFFu;
-    const uint32_t lim = (uint32_t)__builtin_amdgcn_fmed3f(2.0f * ulps + 2.0f, 0.0f, 65536.0f);
-    return dist <= lim || ex < 27u || ex > 227u;
 }
 
 __device__ __forceinline__ void swiglu_bwd_f32(float g, float u, float dh, float& vg, float& vu, bool& redo)
@@ -699,6 +706,26 @@ void launch_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const
     const dim3 grid((unsigned)(F / kGroup), (unsigned)(T / kGroup));
     swiglu_bwd_quant_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up),
                                                   ld, static_cast<const uint16_t*>(dh), T, F, q, s, qT, sT);
+}
+
+// Diagnostic: the fp32 hardware functions the SwiGLU kernels evaluate with,
+// one per element (fn 0: v_exp_f32 = 2^x; fn 1: v_rcp_f32 = 1/x).
+__global__ __launch_bounds__(256) void math_probe_kernel(const float* __restrict__ in, int64_t n,
+                                                         float* __restrict__ out, int fn)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const float x = in[i];
+        out[i] = fn == 0 ? __builtin_amdgcn_exp2f(x) : __builtin_amdgcn_rcpf(x);
+    }
+}
+
+void launch_math_probe(const float* in, int64_t n, float* out, int fn, hipStream_t st)
+{
+    int64_t b = (n + 255) / 256;
+    if (b > 65536)
+        b = 65536;
+    math_probe_kernel<<<(unsigned)(b < 1 ? 1 : b), 256, 0, st>>>(in, n, out, fn);
 }
 
 template <int NP>

@@ -533,6 +533,19 @@ fp8lin_status fp8lin_encode_e4m3(const float* in, int64_t n, uint8_t* out, int m
 fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int method, void* stream);
 
 /*
+ * Diagnostic: the fp32 hardware functions that the SwiGLU kernels
+ * (fp8_swiglu_quant, fp8_swiglu_bwd, fp8_swiglu_bwd_quant) evaluate the
+ * logistic function with, applied to each of n values, so that tests can
+ * measure their error on every argument those kernels pass (the kernels
+ * re-evaluate in fp64 every result that this error could round to a
+ * different BF16):
+ *   fn 0: v_exp_f32, out = 2^in;   fn 1: v_rcp_f32, out = 1 / in.
+ * Buffers are device memory, float [n] each.  n < 0: FP8LIN_ERR_SHAPE;
+ * fn outside 0..1: FP8LIN_ERR_ARG; n == 0 is an OK no-op.
+ */
+fp8lin_status fp8lin_math_probe(const float* in, int64_t n, float* out, int fn, void* stream);
+
+/*
  * Diagnostic: the forward product of fp8_gemm_fwd (Jet-RL summary,
  * "Quantization scheme": FP8 codes, one scale per 128-wide contraction group
  * from 1x128 activation and 128x128 weight quantization) computed by a plain

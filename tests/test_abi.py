@@ -354,6 +354,14 @@ def test_diagnostics_validation(L):
     assert L.fp8lin_encode_e4m3(A, 16, B, 3, s0) == ARG
     assert L.fp8lin_decode_e4m3(A, -1, B, 0, s0) == SHAPE
     assert L.fp8lin_encode_e4m3(None, 0, None, 0, s0) == OK
+    # math probe: in, n, out, fn
+    assert L.fp8lin_math_probe(A, -1, B, 0, s0) == SHAPE
+    assert L.fp8lin_math_probe(A, 16, B, 2, s0) == ARG
+    assert L.fp8lin_math_probe(A, 16, B, -1, s0) == ARG
+    assert L.fp8lin_math_probe(None, 16, B, 0, s0) == NULL
+    assert L.fp8lin_math_probe(A, 16, A, 1, s0) == ALIAS
+    assert L.fp8lin_math_probe(None, 0, None, 1, s0) == OK
+    assert L.fp8lin_math_probe(A, 16, B, 1, s0) == DEVICE
 
 
 @fake_ptrs
