@@ -147,13 +147,14 @@ def test_workload_metric_per_form(case, metrics):
     print(name, json.dumps(res))
     assert res[fl.MFMA_PROBE_FORMS[CONTROL]] <= 1e-2
     assert res["library fp8_gemm_fwd"] <= 1e-2
-    # the four FP8 instructions compute the same sums, bit for bit
-    for form in FP8_FORMS[1:]:
-        assert np.array_equal(outs[form], outs[FP8_FORMS[0]]), form
-    fp8 = res[fl.MFMA_PROBE_FORMS[FP8_FORMS[0]]]
-    if n_out:
-        # with the outlier channels every FP8 form misses the accuracy bound
-        assert fp8 > 1e-2, (name, fp8)
-    else:
-        # without them it meets it: the outlier channels are what breaks FP8
-        assert fp8 <= 1e-2, (name, fp8)
+    # the FP8 instructions' sums agree closely but not always bit for bit (on
+    # one machine they were identical on these data, on another a few
+    # elements in a million differed by an fp32 ulp); each is judged alone
+    for form in FP8_FORMS:
+        fp8 = res[fl.MFMA_PROBE_FORMS[form]]
+        if n_out:
+            # with the outlier channels every FP8 form misses the accuracy bound
+            assert fp8 > 1e-2, (name, form, fp8)
+        else:
+            # without them it meets it: the outlier channels are what breaks FP8
+            assert fp8 <= 1e-2, (name, form, fp8)
