@@ -485,13 +485,18 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
 // s = 1 / (1 + exp(-g)), d_up = dh (g s), d_gate = ((dh u) s) (1 + g (1 - s)),
 // each the fp64 evaluation in that order rounded once to BF16.  As in the
 // forward, the kernel first evaluates in fp32 (eps = 2^-24; dh g and dh u are
-// exact products of BF16 values):
+// exact products of BF16 values), with d_gate written through the identity
+// 1 + g (1 - s) = s z,  z = 1 + e (1 + g):
 //   e = v_exp_f32(g fl(-log2 e))       rel. error <= 2|g| eps + 4 eps
 //   s = v_rcp_f32(1 + e)               <= 2|g| eps + 7 eps
-//   t = e s  (= 1 - s, no cancellation) <= 4|g| eps + 12 eps
-//   q = g t,  w = 1 + q                 w: <= (|q| / |w|) (4|g| + 13) eps + eps
+//   a = 1 + g                          <= eps (exact unless |g| < 2^-16)
+//   z = fma(e, a, 1)                   <= R (2|g| + 5) eps + eps,  R = |e a| / |z|
 //   d_up   = (dh g) s                   <= (2|g| + 8) eps
-//   d_gate = ((dh u) s) w               <= (2|g| + 10 + (|q| / |w|)(4|g| + 13)) eps
+//   d_gate = (((dh u) s) z) s           <= (4|g| + 18 + R (2|g| + 5)) eps
+// z vanishes with silu' (g ~ -1.28) like 1 + g (1 - s) does, but the error it
+// amplifies there is e's alone and R ~ 1 / ((1 + e) |w|): about a tenth of the
+// amplification of the direct form 1 + g t, t = e s, so far fewer results next
+// to that zero need fp64.
 // (exp within 2 ulp and rcp within 1 ulp, measured on every argument these
 // kernels pass).  A relative error of B eps is at most B ulps of the fp32
 // result, so an output whose fp32 bits lie more than B + 2 ulps from a BF16
@@ -511,15 +516,14 @@ __device__ __forceinline__ void swiglu_bwd_f32(float g, float u, float dh, float
 {
     const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
     const float s = __builtin_amdgcn_rcpf(1.0f + e);
-    const float t = e * s;
-    const float q = g * t;
-    const float w = 1.0f + q;
+    const float a = 1.0f + g;
+    const float z = fmaf(e, a, 1.0f);                 // (1 + e) w, one rounding
     vu = (dh * g) * s;
-    vg = ((dh * u) * s) * w;
+    vg = (((dh * u) * s) * z) * s;                    // z before the second s: no intermediate underflow
     const float ag = __builtin_fabsf(g);
-    const float r = __builtin_fabsf(q) * __builtin_amdgcn_rcpf(__builtin_fabsf(w));   // +inf when w = 0
+    const float r = __builtin_fabsf(e * a) * __builtin_amdgcn_rcpf(__builtin_fabsf(z));   // +inf when z = 0
     const float bu = 2.0f * ag + 8.0f;
-    const float bg = 2.0f * ag + 10.0f + r * (4.0f * ag + 13.0f);
+    const float bg = 4.0f * ag + 18.0f + r * (2.0f * ag + 5.0f);
     redo = ag >= 64.0f || !(bg < 65536.0f) || needs_f64(vu, bu) || needs_f64(vg, bg);
 }
 
