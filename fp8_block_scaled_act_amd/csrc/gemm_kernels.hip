@@ -1198,8 +1198,10 @@ struct Cfg {
 };
 // Two workgroups per CU (2 x 66 KB of LDS): while one waits at its step
 // barrier the other computes.  Measured 5-8% ahead of one 256 x 128
-// workgroup of 8 waves with three steps in flight (Cfg<256, 8, 3>), with
-// bit-identical results.
+// workgroup of 8 waves with three steps in flight (Cfg<256, 8, 3>), and
+// level with or ahead of one with two steps in flight (Cfg<256, 8, 2>, 25%
+// fewer operand bytes per flop: 16384 x 27648 x 5120 within 2%, 8192 x
+// 18944 x 3584 6-8% slower), with bit-identical results.
 using Pair = Cfg<128, 4, 2>;
 // Rollout batches (M <= 64) on the batch-invariant forward: 64 x 64 tiles of
 // four waves with one 32 x 32 tile each, so an 8B up-projection fills 224
@@ -1243,6 +1245,7 @@ __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
     using namespace dec;
     using namespace nt;
     static_assert(MODE == Mode::Fwd || MODE == Mode::Wgrad, "NT operands only");
+    static_assert(MODE != Mode::Fwd || 128 % C::BB == 0, "a forward tile's B rows lie in one weight block");
     constexpr int BA = C::BA, BB = C::BB, D = C::D, STAGE = C::STAGE;
     constexpr int OFF_B = C::OFF_B, OFF_SA = C::OFF_SA, OFF_SB = C::OFF_SB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[D * STAGE];
