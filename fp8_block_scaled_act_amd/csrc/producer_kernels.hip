@@ -376,20 +376,22 @@ __device__ __forceinline__ uint32_t swiglu_bf16_f64(float g, float u)
 
 // The fp32 value (rounded to BF16 by the caller) and whether it must be
 // evaluated again in fp64.
-// True when the fp32 value v, within `ulps` ulps of the exact value, may
-// round to a different BF16 than the exact value (a BF16 rounding midpoint
-// lies within ulps + 2 ulps of v; the 2 cover the second-order terms the
-// bounds leave out), or when v lies outside [2^-100, 2^101), where an
-// intermediate could under- or overflow and the relative bounds do not hold.
-// A relative error of B eps (eps = 2^-24) is at most B ulps of the result.
-__device__ __forceinline__ bool needs_f64(float v, float ulps)
+// True when the fp32 value v, within B ulps of the exact value, may round to
+// a different BF16 than the exact value: a BF16 rounding midpoint lies within
+// lim = B + 2 ulps of v (the 2 cover the second-order terms the bounds leave
+// out and the rounding of lim's own evaluation, both far below one ulp), or v
+// lies outside [2^-100, 2^101), where an intermediate could under- or
+// overflow and the relative bounds do not hold.  A relative error of B eps
+// (eps = 2^-24) is at most B ulps of the result.  The conditions are combined
+// without short-circuits so that the test compiles to straight-line code.
+__device__ __forceinline__ bool needs_f64(float v, float lim)
 {
-    // for 0 <= lim <= 2^15: |low 16 bits - 0x8000| <= lim  <=>
-    // (low - 0x8000 + lim) mod 2^16 <= 2 lim (lim = 2^15 flags every value)
-    const uint32_t lim = (uint32_t)__builtin_amdgcn_fmed3f(ulps + 2.0f, 0.0f, 32768.0f);
-    const uint32_t t = (__float_as_uint(v) + lim - 0x8000u) & 0xFFFFu;
+    // the distance in ulps from v to the midpoint of its BF16 interval,
+    // |low 16 bits - 0x8000|: v_sad_u16 adds the absolute differences of both
+    // 16-bit halves, so the high half is cleared first
+    const uint32_t d = __builtin_amdgcn_sad_u16(__float_as_uint(v) & 0xFFFFu, 0x8000u, 0u);
     const float a = __builtin_fabsf(v);
-    return t <= 2u * lim || !(a >= 0x1p-100f && a < 0x1p101f);
+    return ((float)d <= lim) | !((a >= 0x1p-100f) & (a < 0x1p101f));
 }
 
 __device__ __forceinline__ float swiglu_f32(float g, float u, bool& redo)
@@ -397,8 +399,8 @@ __device__ __forceinline__ float swiglu_f32(float g, float u, bool& redo)
     const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
     const float v = (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
     const float ag = __builtin_fabsf(g);
-    const bool exact_zero = g == 0.0f || u == 0.0f;
-    redo = !exact_zero && (ag >= 64.0f || needs_f64(v, 2.0f * ag + 10.0f));
+    const bool exact_zero = (g == 0.0f) | (u == 0.0f);
+    redo = !exact_zero & ((ag >= 64.0f) | needs_f64(v, fmaf(ag, 2.0f, 12.0f)));   // B = 2|g| + 10
     return v;
 }
 
@@ -502,7 +504,7 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
 // result, so an output whose fp32 bits lie more than B + 2 ulps from a BF16
 // midpoint rounds as the exact value does (needs_f64).  The others, |g| >= 64
 // (exponent argument error and exp range), results outside [2^-100, 2^101)
-// (where an intermediate could under- or overflow) and w = 0 are evaluated
+// (where an intermediate could under- or overflow) and z = 0 (R infinite) are evaluated
 // again in fp64, one flagged element at a time per lane.
 __device__ __forceinline__ void swiglu_bwd_f64(float gf, float uf, float df, uint32_t& bg, uint32_t& bu)
 {
@@ -522,9 +524,9 @@ __device__ __forceinline__ void swiglu_bwd_f32(float g, float u, float dh, float
     vg = (((dh * u) * s) * z) * s;                    // z before the second s: no intermediate underflow
     const float ag = __builtin_fabsf(g);
     const float r = __builtin_fabsf(e * a) * __builtin_amdgcn_rcpf(__builtin_fabsf(z));   // +inf when z = 0
-    const float bu = 2.0f * ag + 8.0f;
-    const float bg = 4.0f * ag + 18.0f + r * (2.0f * ag + 5.0f);
-    redo = ag >= 64.0f || !(bg < 65536.0f) || needs_f64(vu, bu) || needs_f64(vg, bg);
+    const float limu = fmaf(ag, 2.0f, 10.0f);                                   // B_u = 2|g| + 8
+    const float limg = fmaf(r, fmaf(ag, 2.0f, 5.0f), fmaf(ag, 4.0f, 20.0f));      // B_g = 4|g| + 18 + R (2|g| + 5)
+    redo = (ag >= 64.0f) | needs_f64(vu, limu) | needs_f64(vg, limg);
 }
 
 // The 8 (d_gate, d_up) pairs of 16-byte chunks of g, u and dh.
