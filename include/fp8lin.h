@@ -20,10 +20,12 @@
  *
  * Conventions for every call:
  *   - All tensors are dense, row-major, on the current HIP device, allocated
- *     and owned by the caller.  The library allocates nothing, keeps no
- *     pointer after it returns and has no mutable global state apart from a
- *     per-device architecture check cached on first use; calls are
- *     thread-safe.
+ *     and owned by the caller.  No call allocates memory or keeps a caller's
+ *     pointer after it returns.  The only mutable global state is per-device
+ *     values cached on first use (the architecture check, and the address of
+ *     the device array of fp8_gemm_fwd_packed_splitk_noalloc); calls are
+ *     thread-safe, apart from that entry point's documented sharing of its
+ *     array.
  *   - BF16 tensors are passed as void* (2 bytes per element); FP8 codes as
  *     uint8_t (one E4M3FN code per byte); scales as float.
  *   - "1x128 scales of an [R,C] tensor" are float [R][C/128]; "128x128 scales"
