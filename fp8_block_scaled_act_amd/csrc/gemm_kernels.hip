@@ -1223,6 +1223,22 @@ struct Sources {
     uint32_t dst_s;                                // its LDS offset within a step
 };
 
+// Waits until this wave's DMA of step g has landed, when `after` later steps
+// (after <= AMAX) have been issued behind it: vmcnt retires in order, so at
+// most after * NDMA of the wave's DMAs may still be outstanding.
+template <int NDMA, int AMAX>
+__device__ __forceinline__ void wait_step(int64_t after)
+{
+    if constexpr (AMAX == 0) {
+        dec::wait_vm<0>();
+    } else {
+        if (after >= AMAX)
+            dec::wait_vm<AMAX * NDMA>();
+        else
+            wait_step<NDMA, AMAX - 1>(after);
+    }
+}
+
 // One wave's share of step g into LDS slot `st` (an LDS byte address).
 template <class C>
 __device__ __forceinline__ void issue_step(const Sources<C>& src, int wave, uint32_t st, int64_t g)
@@ -1309,10 +1325,8 @@ __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
         if (s0 < G)
             issue_step<C>(src, wave, base + s0 * STAGE, s0);
     for (int64_t g = 0; g < G; ++g) {
-        if (g + 1 < G)
-            wait_vm<(D - 2) * C::NDMA>();          // step g landed (this wave's part)
-        else
-            wait_vm<0>();
+        // steps g + 1 .. min(g + D - 2, G - 1) were issued behind step g
+        wait_step<C::NDMA, D - 2>(G - 1 - g);      // step g landed (this wave's part)
         __syncthreads();                           // all of step g landed; step g - 1 retired
         if (g + D - 1 < G)
             issue_step<C>(src, wave, base + (uint32_t)(((g + D - 1) % D) * STAGE), g + D - 1);

@@ -290,6 +290,27 @@ def test_fwd_unified_bitwise_full_decode_shape():
         assert np.array_equal(run(a, b), y_all[a:b]), (a, b)
 
 
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 640])
+def test_fwd_unified_short_contractions(K):
+    """The 64 x 64 tiles keep four steps in flight; with fewer groups than that
+    (K = 128 .. 384) and on the last steps of a longer contraction, each step
+    must still be waited for before it is read.  Ten repeated 64-row and 5-row
+    calls give the bits of the 128 x 128 tiles' rows, with every call's output
+    prefilled with a different pattern."""
+    M, N = 192, 8192
+    xq, sx = codes_scales((M, K), (M, K // G), K + 3, 17)
+    wq, sw = codes_scales((N, K), (N // G, K // G), K + 4, 18)
+    dw, dsw = u8_to_dev(wq), f32_to_dev(sw)
+    say("gemm_fwd_unified short contraction K =", K)
+    y_all = host(fl.fp8_gemm_fwd(u8_to_dev(xq), f32_to_dev(sx), dw, dsw))
+    for a, b in ((64, 128), (100, 105)):
+        xa, sa = u8_to_dev(xq[a:b]), f32_to_dev(sx[a:b])
+        for rep in range(10):
+            out = torch.full((b - a, N), float(rep - 5), dtype=torch.bfloat16, device=DEV)
+            got = host(fl.fp8_gemm_fwd_unified(xa, sa, dw, dsw, out=out))
+            assert np.array_equal(got, y_all[a:b]), (K, a, b, rep)
+
+
 @pytest.mark.parametrize("kind,M,N,K", [("fwd", 64, 14336, 4096), ("fwd", 300, 1024, 1024),
                                         ("dgrad", 300, 1024, 512), ("wgrad", 512, 384, 1024)])
 def test_gemm_deterministic(kind, M, N, K):
