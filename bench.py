@@ -718,8 +718,9 @@ def main():
                     help="turn FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the layer would "
+              "shard by token rows, 128-aligned, with one all-reduce of the weight gradients); "
+              "run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

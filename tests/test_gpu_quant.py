@@ -18,7 +18,6 @@ from gpu_util import DEV, bf16_to_dev, f32_to_dev, first_mismatch, host, say, u8
 
 pytestmark = pytest.mark.gpu
 G = 128
-OUT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
 
 
 def check_quant(q_gpu, s_gpu, q_ref, s_ref, what):
@@ -57,12 +56,15 @@ def _oracle_encode_many():
 
 
 def test_encoder_exhaustive_all_fp32():
-    """The kernels' encoder (method 0) equals the oracle on every finite fp32
-    bit pattern.  The hardware conversion (method 1) is measured on the same
-    inputs and its disagreements are recorded (informational)."""
+    """The kernels' encoder (method 0: the hardware conversion on inputs
+    clamped to +-448) equals the oracle on every finite fp32 bit pattern.  The
+    unclamped hardware conversion (method 1) must agree with the oracle for
+    every |v| <= 464: the fast quotient reaches 448 (1 + 2^-23) unclamped, and
+    464 is the midpoint that rounds to 448.  Above 464 it returns the NaN code
+    (counted, not an error: no kernel passes such values)."""
     enc = _oracle_encode_many()
     chunk = 1 << 28
-    stats = {"hw_mismatch_total": 0, "hw_mismatch_le448": 0, "hw_examples": []}
+    stats = {"hw_mismatch_total": 0, "hw_mismatch_le464": 0, "hw_examples": []}
     for c in range((1 << 32) // chunk):
         lo = c * chunk
         say("encoder exhaustive chunk", c, "of", (1 << 32) // chunk)
@@ -82,14 +84,12 @@ def test_encoder_exhaustive_all_fp32():
         stats["hw_mismatch_total"] += int(hw_bad.size)
         if hw_bad.size:
             mags = np.abs(hb[hw_bad].view(np.float32))
-            stats["hw_mismatch_le448"] += int(np.sum(mags <= 448.0))
+            stats["hw_mismatch_le464"] += int(np.sum(mags <= 464.0))
             for i in hw_bad[:: max(1, hw_bad.size // 4)][:4]:
                 stats["hw_examples"].append([hex(int(hb[i])), float(hb[i:i + 1].view(np.float32)[0]),
                                              hex(int(q1[i])), hex(int(ref[i]))])
     print("hardware cvt vs definition:", json.dumps(stats))
-    os.makedirs(OUT, exist_ok=True)
-    with open(os.path.join(OUT, "probe_hw_cvt_encode.json"), "w") as f:
-        json.dump(stats, f, indent=1)
+    assert stats["hw_mismatch_le464"] == 0, stats["hw_examples"]
 
 
 def test_decoder_all_codes():
@@ -104,9 +104,7 @@ def test_decoder_all_codes():
     mism = [(hex(int(c)), float(h), float(r)) for c, h, r in zip(codes, hw, ref)
             if np.float32(h).view(np.uint32) != np.float32(r).view(np.uint32)]
     print("hardware decode mismatches:", len(mism), mism[:8])
-    os.makedirs(OUT, exist_ok=True)
-    with open(os.path.join(OUT, "probe_hw_cvt_decode.json"), "w") as f:
-        json.dump({"mismatches": len(mism), "examples": mism[:16]}, f, indent=1)
+    assert not mism, mism[:8]
 
 
 # ----------------------------------------------------------- 1x128 groups
