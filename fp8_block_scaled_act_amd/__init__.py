@@ -28,6 +28,7 @@ __all__ = [
     "fp8_mxfp4_quant_weight", "fp8_gemm_fwd_w4",
     "fp8lin_encode_e4m3", "fp8lin_decode_e4m3", "fp8lin_gemm_fwd_mfma_probe", "MFMA_PROBE_FORMS",
     "fp8lin_math_probe",
+    "fp8lin_flag_probe",
     "SRC_BF16", "SRC_FP8_ROWQ",
 ]
 
@@ -90,6 +91,8 @@ _SYMBOLS = {
     "fp8lin_gemm_fwd_mfma_probe": ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 +
                                    [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p], ctypes.c_int),
     "fp8lin_math_probe": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p],
+                          ctypes.c_int),
+    "fp8lin_flag_probe": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p],
                           ctypes.c_int),
 }
 
@@ -694,6 +697,16 @@ def fp8lin_math_probe(x: torch.Tensor, fn: int, out=None, stream=None):
     y = out if out is not None else torch.empty(x.shape, dtype=torch.float32, device=x.device)
     _expect(y, "out", torch.float32, tuple(x.shape))
     _check(lib().fp8lin_math_probe(_ptr(x), x.numel(), _ptr(y), int(fn), _stream(stream)), "fp8lin_math_probe")
+    return y
+
+
+def fp8lin_flag_probe(v: torch.Tensor, lim: float, out=None, stream=None):
+    """The SwiGLU kernels' fp64 re-evaluation test on a flat float32 tensor
+    with bound lim (fp32 ulps): 1.0 where it flags the value, else 0.0."""
+    _expect(v, "v", torch.float32, tuple(v.shape))
+    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    _expect(y, "out", torch.float32, tuple(v.shape))
+    _check(lib().fp8lin_flag_probe(_ptr(v), v.numel(), float(lim), _ptr(y), _stream(stream)), "fp8lin_flag_probe")
     return y
 
 

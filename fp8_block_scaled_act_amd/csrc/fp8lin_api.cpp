@@ -875,6 +875,26 @@ fp8lin_status fp8lin_math_probe(const float* in, int64_t n, float* out, int fn, 
     return end_launch();
 }
 
+fp8lin_status fp8lin_flag_probe(const float* v, int64_t n, float lim, float* out, void* stream)
+{
+    if (n < 0)
+        return FP8LIN_ERR_SHAPE;
+    int64_t b;
+    if (!mul_ok(n, 4, &b))
+        return FP8LIN_ERR_SHAPE;
+    const Buf ib[] = {{v, b}};
+    const Buf ob[] = {{out, b}};
+    fp8lin_status s = check_buffers(ib, 1, ob, 1);
+    if (s != FP8LIN_OK)
+        return s;
+    if (n == 0)
+        return FP8LIN_OK;
+    if ((s = begin_launch()) != FP8LIN_OK)
+        return s;
+    fp8lin::launch_flag_probe(v, n, lim, out, as_stream(stream));
+    return end_launch();
+}
+
 fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int method, void* stream)
 {
     if (n < 0)

@@ -23,6 +23,7 @@ void launch_gemm_fwd_mfma_probe(const uint8_t* xq, const float* sx, const uint8_
 void launch_encode_probe(const float* in, int64_t n, uint8_t* out, int method, hipStream_t st);
 void launch_decode_probe(const uint8_t* in, int64_t n, float* out, int method, hipStream_t st);
 void launch_math_probe(const float* in, int64_t n, float* out, int fn, hipStream_t st);
+void launch_flag_probe(const float* v, int64_t n, float lim, float* out, hipStream_t st);
 
 // Producer operators fused with 1x128 quantization (K <= 16384 for RMSNorm).
 void launch_rmsnorm_quant(const void* x, const void* gamma, int64_t M, int64_t K, float eps, uint8_t* q,

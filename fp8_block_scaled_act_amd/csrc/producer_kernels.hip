@@ -734,6 +734,24 @@ void launch_math_probe(const float* in, int64_t n, float* out, int fn, hipStream
     math_probe_kernel<<<(unsigned)(b < 1 ? 1 : b), 256, 0, st>>>(in, n, out, fn);
 }
 
+// Diagnostic: the SwiGLU kernels' re-evaluation test (needs_f64) on given
+// values with one bound, 1.0 where it flags the value, else 0.0.
+__global__ __launch_bounds__(256) void flag_probe_kernel(const float* __restrict__ v, int64_t n, float lim,
+                                                         float* __restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+        out[i] = needs_f64(v[i], lim) ? 1.0f : 0.0f;
+}
+
+void launch_flag_probe(const float* v, int64_t n, float lim, float* out, hipStream_t st)
+{
+    int64_t b = (n + 255) / 256;
+    if (b > 65536)
+        b = 65536;
+    flag_probe_kernel<<<(unsigned)(b < 1 ? 1 : b), 256, 0, st>>>(v, n, lim, out);
+}
+
 template <int NP>
 static void rmsnorm_bwd_dx_launch(const uint16_t* x, const uint16_t* g, const float* r, const uint16_t* dy, int64_t M,
                                   int K, uint16_t* dx, hipStream_t st)

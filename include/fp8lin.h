@@ -548,6 +548,18 @@ fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int m
 fp8lin_status fp8lin_math_probe(const float* in, int64_t n, float* out, int fn, void* stream);
 
 /*
+ * Diagnostic: the test by which the SwiGLU kernels decide to re-evaluate an
+ * fp32 result in fp64, applied to each of n values v with one bound lim (in
+ * fp32 ulps), so that tests can check it against its definition on every bit
+ * pattern: out[i] = 1.0 when a BF16 rounding midpoint lies within lim ulps of
+ * v[i] (|low 16 bits of v[i] - 0x8000| <= lim) or |v[i]| is outside
+ * [2^-100, 2^101) (NaN included), else 0.0.
+ * Buffers are device memory, float [n] each.  n < 0: FP8LIN_ERR_SHAPE;
+ * n == 0 is an OK no-op.
+ */
+fp8lin_status fp8lin_flag_probe(const float* v, int64_t n, float lim, float* out, void* stream);
+
+/*
  * Diagnostic: the forward product of fp8_gemm_fwd (Jet-RL summary,
  * "Quantization scheme": FP8 codes, one scale per 128-wide contraction group
  * from 1x128 activation and 128x128 weight quantization) computed by a plain

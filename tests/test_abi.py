@@ -362,6 +362,13 @@ def test_diagnostics_validation(L):
     assert L.fp8lin_math_probe(A, 16, A, 1, s0) == ALIAS
     assert L.fp8lin_math_probe(None, 0, None, 1, s0) == OK
     assert L.fp8lin_math_probe(A, 16, B, 1, s0) == DEVICE
+    # re-evaluation test probe: v, n, lim, out
+    assert L.fp8lin_flag_probe(A, -1, 12.0, B, s0) == SHAPE
+    assert L.fp8lin_flag_probe(None, 16, 12.0, B, s0) == NULL
+    assert L.fp8lin_flag_probe(A, 16, 12.0, None, s0) == NULL
+    assert L.fp8lin_flag_probe(A, 16, 12.0, A, s0) == ALIAS
+    assert L.fp8lin_flag_probe(None, 0, 12.0, None, s0) == OK
+    assert L.fp8lin_flag_probe(A, 16, 12.0, B, s0) == DEVICE
 
 
 @fake_ptrs

@@ -11,7 +11,10 @@ midpoint.  That bound assumes v_exp_f32 within 2 ulp and v_rcp_f32 within
   - v_rcp_f32 on every fp32 d in [1, 2^93) (d = fl(1 + e) with
     e = exp2(g * c) < 2^92.34).
 The reference is the function in fp64 (torch on the device), the error is in
-ulps of the fp32 result (spacing at the reference's binade)."""
+ulps of the fp32 result (spacing at the reference's binade).  The test that
+decides the re-evaluation is checked against its definition on every low half
+of the fp32 bits."""
+import numpy as np
 import pytest
 import torch
 
@@ -70,3 +73,34 @@ def test_rcp_within_1_ulp_on_the_kernels_arguments():
         worst = max(worst, max_ulp_error(got, ref))
     say("v_rcp_f32 max error %.4f ulp" % worst)
     assert worst <= 1.0
+
+
+# the fp32 high halves the flag test is checked under: ordinary values of both
+# signs, the edges of [2^-100, 2^101), zeros and subnormals, the largest
+# finite values, infinities and NaNs
+HIGH_HALVES = [0x3F80, 0xBF80, 0x4B00, 0x3380, 0x0D80, 0x0D7F, 0x8D80, 0x7200, 0x71FF, 0xF1FF,
+               0x0000, 0x8000, 0x0040, 0x7F7F, 0x7F80, 0xFF80, 0x7FC0]
+LIMS = [0.0, 1.0, 11.5, 12.0, 140.0, 32767.0, 32768.0, 65536.0, float("inf")]
+
+
+def test_reevaluation_flag_matches_its_definition():
+    """The SwiGLU kernels' test for an fp64 re-evaluation flags exactly the
+    values with a BF16 rounding midpoint within lim ulps (|low 16 bits -
+    0x8000| <= lim) or a magnitude outside [2^-100, 2^101) (NaN included), on
+    every low half under each high half above and each bound."""
+    low = np.arange(1 << 16, dtype=np.uint32)
+    dist = np.abs(low.astype(np.int64) - 0x8000)
+    for hi in HIGH_HALVES:
+        bits = (np.uint32(hi) << np.uint32(16)) | low
+        v = bits.view(np.float32)
+        with np.errstate(invalid="ignore"):
+            a = np.abs(v.astype(np.float64))
+            outside = ~((a >= 2.0 ** -100) & (a < 2.0 ** 101))
+        vd = torch.from_numpy(v.copy()).to(DEV)
+        for lim in LIMS:
+            want = (dist <= lim) | outside
+            got = fl.fp8lin_flag_probe(vd, lim).cpu().numpy() != 0
+            bad = np.nonzero(got != want)[0]
+            assert bad.size == 0, "high %#06x lim %g: bits %#010x flagged %s, expected %s" % (
+                hi, lim, bits[bad[0]], got[bad[0]], want[bad[0]])
+    say("re-evaluation flag: %d high halves x %d bounds, every low half" % (len(HIGH_HALVES), len(LIMS)))
