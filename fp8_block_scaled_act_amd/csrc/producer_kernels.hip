@@ -523,10 +523,17 @@ __device__ __forceinline__ void swiglu_bwd_f32(float g, float u, float dh, float
     vu = (dh * g) * s;
     vg = (((dh * u) * s) * z) * s;                    // z before the second s: no intermediate underflow
     const float ag = __builtin_fabsf(g);
-    const float r = __builtin_fabsf(e * a) * __builtin_amdgcn_rcpf(__builtin_fabsf(z));   // +inf when z = 0
     const float limu = fmaf(ag, 2.0f, 10.0f);                                   // B_u = 2|g| + 8
-    const float limg = fmaf(r, fmaf(ag, 2.0f, 5.0f), fmaf(ag, 4.0f, 20.0f));      // B_g = 4|g| + 18 + R (2|g| + 5)
-    redo = (ag >= 64.0f) | needs_f64(vu, limu) | needs_f64(vg, limg);
+    // d_gate's test without a reciprocal: with lim = B_g + 2 = Y + R X,
+    // R = |e a| / |z|, a midpoint distance d satisfies d <= lim exactly when
+    // (d - Y) |z| <= |e a| X (z = 0: always, as R is infinite).  The three
+    // roundings of that comparison move it by far less than the 2-ulp margin.
+    const float X = fmaf(ag, 2.0f, 5.0f), Y = fmaf(ag, 4.0f, 20.0f);
+    const float dg = (float)__builtin_amdgcn_sad_u16(__float_as_uint(vg) & 0xFFFFu, 0x8000u, 0u);
+    const float avg = __builtin_fabsf(vg);
+    const bool near_g = (dg - Y) * __builtin_fabsf(z) <= __builtin_fabsf(e * a) * X;
+    const bool out_g = !((avg >= 0x1p-100f) & (avg < 0x1p101f));
+    redo = (ag >= 64.0f) | needs_f64(vu, limu) | near_g | out_g;
 }
 
 // The 8 (d_gate, d_up) pairs of 16-byte chunks of g, u and dh.
