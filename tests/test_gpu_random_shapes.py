@@ -90,3 +90,76 @@ def test_random_shapes(seed):
     bT, sbT = synthetic.random_codes((Kw, Tw), seed, 29), synthetic.random_scales((Kw, Tw // G), seed, 30)
     within_metric(fl.fp8_gemm_wgrad(u8_to_dev(aT), f32_to_dev(saT), u8_to_dev(bT), f32_to_dev(sbT)),
                   oracle.gemm_wgrad(aT, saT, bT, sbT), "wgrad %dx%dx%d" % (Nw, Kw, Tw))
+
+
+@pytest.mark.parametrize("seed", range(9100, 9132))
+def test_random_shapes_rollout_and_fused(seed):
+    """The rollout GEMMs (decode layout, split over K with a workspace and
+    without), 4-bit weights, the FP8-source transpose, DGrad on the transposed
+    weight, and the one-call linear and MLP forward against their parts."""
+    r = np.random.default_rng(seed)
+    say("random shapes (rollout and fused), seed", seed)
+    # decode layout and split-K: M <= 64, K % 256 == 0
+    M, N, K = int(r.integers(1, 65)), G * int(r.integers(1, 40)), 256 * int(r.integers(1, 24))
+    xq, sx = synthetic.random_codes((M, K), seed, 41), synthetic.random_scales((M, K // G), seed, 42)
+    wq, sw = synthetic.random_codes((N, K), seed, 43), synthetic.random_scales((N // G, K // G), seed, 44)
+    ref = oracle.gemm_fwd(xq, sx, wq, sw)
+    dx, dsx, dw, dsw = u8_to_dev(xq), f32_to_dev(sx), u8_to_dev(wq), f32_to_dev(sw)
+    wp = fl.fp8_weight_pack(dw)
+    y_packed = fl.fp8_gemm_fwd_packed(dx, dsx, wp, dsw)
+    within_metric(y_packed, ref, "packed %dx%dx%d" % (M, N, K))
+    same(host(y_packed), host(fl.fp8_gemm_fwd(dx, dsx, dw, dsw)), "packed vs unpacked bits")
+    y_split = fl.fp8_gemm_fwd_packed_splitk(dx, dsx, wp, dsw)
+    within_metric(y_split, ref, "split-K %dx%dx%d" % (M, N, K))
+    if fl.fp8_gemm_fwd_packed_splitk_workspace(M, N, K) <= 4 << 20:
+        same(host(fl.fp8_gemm_fwd_packed_splitk_noalloc(dx, dsx, wp, dsw)), host(y_split), "noalloc vs workspace")
+
+    # 4-bit weights: quantizer bit-exact, GEMM within the metric
+    N4, K4 = int(r.integers(1, 300)), G * int(r.integers(1, 40))
+    w = synthetic.weights(N4, K4, seed=seed, sigma=float(10.0 ** r.uniform(-3, 0)))
+    c4, s4 = fl.fp8_mxfp4_quant_weight(bf16_to_dev(w))
+    oc4, os4 = oracle.mxfp4_quant(w)
+    same(host(c4), oc4, "mxfp4 codes %dx%d" % (N4, K4))
+    same(host(s4), os4, "mxfp4 scales")
+    M4 = int(r.integers(1, 200))
+    xq4, sx4 = synthetic.random_codes((M4, K4), seed, 45), synthetic.random_scales((M4, K4 // G), seed, 46)
+    within_metric(fl.fp8_gemm_fwd_w4(u8_to_dev(xq4), f32_to_dev(sx4), c4, s4), oracle.gemm_fwd_w4(xq4, sx4, oc4, os4),
+                  "w4 %dx%dx%d" % (M4, N4, K4))
+
+    # transpose of saved FP8 activations; DGrad on the transposed weight
+    T, C = G * int(r.integers(1, 5)), G * int(r.integers(1, 10))
+    xa = synthetic.activations(T, C, seed=seed + 2000, n_out=2)
+    q, s = fl.fp8_quant_act(bf16_to_dev(xa))
+    qT, sT = fl.fp8_quant_transpose(q, s)
+    oqT, osT = oracle.quant_transpose_fp8(host(q), host(s))
+    same(host(qT), oqT, "quant_transpose fp8 %dx%d" % (T, C))
+    same(host(sT).view(np.uint32), osT.view(np.uint32), "quant_transpose fp8 scales")
+    Nd, Kd, Td = G * int(r.integers(1, 8)), G * int(r.integers(1, 8)), int(r.integers(1, 300))
+    wd, swd = synthetic.random_codes((Nd, Kd), seed, 47), synthetic.random_scales((Nd // G, Kd // G), seed, 48)
+    wdT, swdT = fl.fp8_weight_transpose(u8_to_dev(wd), f32_to_dev(swd))
+    same(host(wdT), wd.T, "weight transpose codes")
+    same(host(swdT).view(np.uint32), np.ascontiguousarray(swd.T).view(np.uint32), "weight transpose scales")
+    dyq, sdy = synthetic.random_codes((Td, Nd), seed, 49), synthetic.random_scales((Td, Nd // G), seed, 50)
+    within_metric(fl.fp8_gemm_dgrad_t(u8_to_dev(dyq), f32_to_dev(sdy), wdT, swdT), oracle.gemm_dgrad(dyq, sdy, wd, swd),
+                  "dgrad_t %dx%dx%d" % (Td, Nd, Kd))
+
+    # one-call forms, bit-identical to the calls they enqueue
+    Ml, Kl, Nl = int(r.integers(1, 200)), G * int(r.integers(1, 16)), G * int(r.integers(1, 8))
+    xl = bf16_to_dev(synthetic.activations(Ml, Kl, seed=seed + 3000, n_out=1))
+    wl, swl = u8_to_dev(synthetic.random_codes((Nl, Kl), seed, 51)), f32_to_dev(synthetic.random_scales((Nl // G, Kl // G), seed, 52))
+    y, ql, sl = fl.fp8_linear_fwd(xl, wl, swl)
+    q2, s2 = fl.fp8_quant_act(xl)
+    same(host(ql), host(q2), "linear_fwd codes")
+    same(host(y), host(fl.fp8_gemm_fwd(q2, s2, wl, swl)), "linear_fwd output")
+    Tm, Km, Fm = int(r.integers(1, 160)), G * int(r.integers(1, 12)), G * int(r.integers(1, 12))
+    xm = bf16_to_dev(synthetic.activations(Tm, Km, seed=seed + 4000, n_out=1))
+    gm = bf16_to_dev(synthetic.norm_weights(Km, seed=seed))
+    wgu, sgu = fl.fp8_quant_weight(bf16_to_dev(synthetic.weights(2 * Fm, Km, seed=seed + 1)))
+    wdn, sdn = fl.fp8_quant_weight(bf16_to_dev(synthetic.weights(Km, Fm, seed=seed + 2)))
+    o = fl.fp8_mlp_fwd(xm, gm, wgu, sgu, wdn, sdn)
+    xq1, sx1, r1 = fl.fp8_rmsnorm_quant(xm, gm)
+    gu1 = fl.fp8_gemm_fwd(xq1, sx1, wgu, sgu)
+    hq1, sh1 = fl.fp8_swiglu_quant(gu1[:, :Fm], gu1[:, Fm:])
+    for name, a, b in (("xq", o["xq"], xq1), ("rstd", o["rstd"], r1), ("gu", o["gu"], gu1), ("hq", o["hq"], hq1),
+                       ("sh", o["sh"], sh1), ("y", o["y"], fl.fp8_gemm_fwd(hq1, sh1, wdn, sdn))):
+        same(host(a).view(np.uint8), host(b).view(np.uint8), "mlp_fwd %s (%dx%dx%d)" % (name, Tm, Km, Fm))
