@@ -1,7 +1,8 @@
 """Randomized parity: for each seed, random shapes and value scales drawn
-from the seed, every quantizer and producer bit-exact against the CPU oracle
-(near-tie elements of the SwiGLU forms checked against both valid roundings)
-and every GEMM form within the 1e-2 metric.  The fixed-shape tests pin the
+from the seed, every quantizer and producer (forward and backward)
+bit-exact against the CPU oracle (near-tie elements of the SwiGLU forms
+checked against both valid roundings) and every GEMM form within the 1e-2
+metric.  The fixed-shape tests pin the
 workloads' sizes and the edge cases; this tier covers the shapes between
 them (ragged rows, any number of 128-groups, scales from 1e-4 to 1)."""
 import numpy as np
@@ -12,7 +13,7 @@ import oracle
 import synthetic
 from gpu_util import bf16_bits_to_f64, bf16_to_dev, f32_to_dev, first_mismatch, host, say, u8_to_dev
 from test_gpu_mlp_bwd import check_swiglu_bwd_quant, compare_swiglu_bwd
-from test_gpu_producers import compare_swiglu, gamma_for, run_rmsnorm
+from test_gpu_producers import compare_swiglu, gamma_for, run_rmsnorm, run_rmsnorm_bwd
 
 pytestmark = pytest.mark.gpu
 G = 128
@@ -60,6 +61,8 @@ def test_random_shapes(seed):
     Mr, Kr = int(r.integers(1, 200)), G * int(r.integers(1, 64))
     run_rmsnorm(synthetic.activations(Mr, Kr, seed=seed + 7, n_out=int(r.integers(0, 4))), gamma_for(Kr, seed),
                 float(r.choice([1e-6, 1e-5, 0.0])), "random %d" % seed)
+    Mb, Kb = int(r.integers(1, 400)), G * int(r.integers(1, 64))
+    run_rmsnorm_bwd(Mb, Kb, seed, "random %d" % seed, with_dgamma=bool(r.integers(0, 4)))
     Ms, F = int(r.integers(1, 160)), G * int(r.integers(1, 24))
     gate = synthetic.gaussian_bf16((Ms, F), float(r.uniform(0.3, 6.0)), seed, 11)
     up = synthetic.gaussian_bf16((Ms, F), float(r.uniform(0.1, 3.0)), seed, 12)
