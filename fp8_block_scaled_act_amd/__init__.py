@@ -691,8 +691,9 @@ def fp8lin_decode_e4m3(q: torch.Tensor, method: int = 0, out=None, stream=None):
 
 
 def fp8lin_math_probe(x: torch.Tensor, fn: int, out=None, stream=None):
-    """Device fp32 hardware function on a flat float32 tensor: fn 0 = 2^x
-    (v_exp_f32), fn 1 = 1/x (v_rcp_f32)."""
+    """Device fp32 function on a flat float32 tensor: fn 0 = 2^x (v_exp_f32),
+    fn 1 = 1/x (v_rcp_f32), fn 2 = x/448 and fn 3 = 1/x as the quantizers form
+    their group scale and reciprocal without a division."""
     _expect(x, "in", torch.float32, tuple(x.shape))
     y = out if out is not None else torch.empty(x.shape, dtype=torch.float32, device=x.device)
     _expect(y, "out", torch.float32, tuple(x.shape))

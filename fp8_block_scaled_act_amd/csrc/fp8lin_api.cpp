@@ -857,7 +857,7 @@ fp8lin_status fp8lin_math_probe(const float* in, int64_t n, float* out, int fn, 
 {
     if (n < 0)
         return FP8LIN_ERR_SHAPE;
-    if (fn < 0 || fn > 1)
+    if (fn < 0 || fn > 3)
         return FP8LIN_ERR_ARG;
     int64_t b;
     if (!mul_ok(n, 4, &b))

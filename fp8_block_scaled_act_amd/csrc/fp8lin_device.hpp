@@ -96,8 +96,9 @@ __device__ __forceinline__ uint32_t max_over_64_lanes(uint32_t v)
 
 // --------------------------------------------------------- group scaling
 
-// Per-group quantities.  s = fp32(amax / 448) and r = fp32(1 / s), both by
-// IEEE division.  `fast` selects the quotient route below.
+// Per-group quantities.  s = fp32(amax / 448) and r = fp32(1 / s), both
+// correctly rounded (the quotients IEEE division gives).  `fast` selects the
+// quotient route below.
 struct GroupScale {
     float s;
     float r;
@@ -109,13 +110,39 @@ struct GroupScale {
 // signed-zero code.  Smaller scales (amax < ~2^-83) take IEEE division.
 constexpr float kFastScaleMin = 0x1p-92f;
 
+// fp32(a / 448) without a division, for a in [2^-100, 2^128): 448 = 7 * 2^6,
+// so a / 448 = fp32(a / 7) * 2^-6 exactly while that product is normal (it
+// is at least 2^-109 here), and fp32(a / 7) is q = fp32(a * fp32(1/7))
+// corrected once, fp32(q + (a - 7 q) * fp32(1/7)) with both steps fused (the
+// residual is exact).  Checked against IEEE division on every such a.
+__device__ __forceinline__ float div448_rn(float a)
+{
+    constexpr float c = 1.0f / 7.0f;
+    const float q = a * c;
+    return __builtin_amdgcn_ldexpf(fmaf(fmaf(-q, 7.0f, a), c, q), -6);
+}
+
+// fp32(1 / s) without a division, for s in [2^-92, 2^120): one Newton step
+// y + y (1 - s y) on v_rcp_f32's estimate, both steps fused.  Checked against
+// IEEE division on every such s.
+__device__ __forceinline__ float rcp_rn(float s)
+{
+    const float y = __builtin_amdgcn_rcpf(s);
+    return fmaf(fmaf(-s, y, 1.0f), y, y);
+}
+
 __device__ __forceinline__ GroupScale group_scale(uint32_t amax_bits)
 {
     GroupScale g;
-    float a = __uint_as_float(amax_bits);
-    g.s = a / 448.0f;
-    g.r = 1.0f / g.s;
+    const float a = __uint_as_float(amax_bits);
+    const bool tiny = !(a >= 0x1p-100f);
+    g.s = div448_rn(a);
+    if (__builtin_amdgcn_ballot_w64(tiny) != 0)   // rare: the IEEE division only where needed
+        if (tiny)
+            g.s = a / 448.0f;
     g.fast = g.s >= kFastScaleMin;
+    // r is read only by the fast quotient (s >= 2^-92; s < 2^120 for any finite amax)
+    g.r = rcp_rn(g.s);
     if (amax_bits == 0) {                  // all-zero group: scale 0, codes = signs
         g.s = 0.0f;
         g.r = 0.0f;

@@ -722,14 +722,19 @@ void launch_swiglu_bwd_quant(const void* gate, const void* up, int64_t ld, const
 }
 
 // Diagnostic: the fp32 hardware functions the SwiGLU kernels evaluate with,
-// one per element (fn 0: v_exp_f32 = 2^x; fn 1: v_rcp_f32 = 1/x).
+// and the division-free group-scale functions of the quantizers, one per
+// element (fn 0: v_exp_f32 = 2^x; fn 1: v_rcp_f32 = 1/x; fn 2: div448_rn;
+// fn 3: rcp_rn).
 __global__ __launch_bounds__(256) void math_probe_kernel(const float* __restrict__ in, int64_t n,
                                                          float* __restrict__ out, int fn)
 {
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
         const float x = in[i];
-        out[i] = fn == 0 ? __builtin_amdgcn_exp2f(x) : __builtin_amdgcn_rcpf(x);
+        out[i] = fn == 0 ? __builtin_amdgcn_exp2f(x)
+                 : fn == 1 ? __builtin_amdgcn_rcpf(x)
+                 : fn == 2 ? div448_rn(x)
+                           : rcp_rn(x);
     }
 }
 

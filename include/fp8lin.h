@@ -537,13 +537,17 @@ fp8lin_status fp8lin_decode_e4m3(const uint8_t* in, int64_t n, float* out, int m
 /*
  * Diagnostic: the fp32 hardware functions that the SwiGLU kernels
  * (fp8_swiglu_quant, fp8_swiglu_bwd, fp8_swiglu_bwd_quant) evaluate the
- * logistic function with, applied to each of n values, so that tests can
- * measure their error on every argument those kernels pass (the kernels
- * re-evaluate in fp64 every result that this error could round to a
- * different BF16):
- *   fn 0: v_exp_f32, out = 2^in;   fn 1: v_rcp_f32, out = 1 / in.
+ * logistic function with, and the division-free functions every quantizer
+ * forms its group scale and reciprocal with, applied to each of n values, so
+ * that tests can check them on every argument the kernels pass (the SwiGLU
+ * kernels re-evaluate in fp64 every result that the first two functions'
+ * error could round to a different BF16; the last two must equal the
+ * correctly rounded quotient):
+ *   fn 0: v_exp_f32, out = 2^in;   fn 1: v_rcp_f32, out = 1 / in;
+ *   fn 2: out = fp32(in / 448) for in in [2^-100, 2^128);
+ *   fn 3: out = fp32(1 / in) for in in [2^-92, 2^120).
  * Buffers are device memory, float [n] each.  n < 0: FP8LIN_ERR_SHAPE;
- * fn outside 0..1: FP8LIN_ERR_ARG; n == 0 is an OK no-op.
+ * fn outside 0..3: FP8LIN_ERR_ARG; n == 0 is an OK no-op.
  */
 fp8lin_status fp8lin_math_probe(const float* in, int64_t n, float* out, int fn, void* stream);
 

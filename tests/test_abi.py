@@ -356,7 +356,7 @@ def test_diagnostics_validation(L):
     assert L.fp8lin_encode_e4m3(None, 0, None, 0, s0) == OK
     # math probe: in, n, out, fn
     assert L.fp8lin_math_probe(A, -1, B, 0, s0) == SHAPE
-    assert L.fp8lin_math_probe(A, 16, B, 2, s0) == ARG
+    assert L.fp8lin_math_probe(A, 16, B, 4, s0) == ARG
     assert L.fp8lin_math_probe(A, 16, B, -1, s0) == ARG
     assert L.fp8lin_math_probe(None, 16, B, 0, s0) == NULL
     assert L.fp8lin_math_probe(A, 16, A, 1, s0) == ALIAS

@@ -13,7 +13,8 @@ midpoint.  That bound assumes v_exp_f32 within 2 ulp and v_rcp_f32 within
 The reference is the function in fp64 (torch on the device), the error is in
 ulps of the fp32 result (spacing at the reference's binade).  The test that
 decides the re-evaluation is checked against its definition on every low half
-of the fp32 bits."""
+of the fp32 bits, and the division-free group scale and reciprocal of the
+quantizers against correct rounding on every argument in their ranges."""
 import numpy as np
 import pytest
 import torch
@@ -104,3 +105,45 @@ def test_reevaluation_flag_matches_its_definition():
             assert bad.size == 0, "high %#06x lim %g: bits %#010x flagged %s, expected %s" % (
                 hi, lim, bits[bad[0]], got[bad[0]], want[bad[0]])
     say("re-evaluation flag: %d high halves x %d bounds, every low half" % (len(HIGH_HALVES), len(LIMS)))
+
+
+def _correctly_rounded(y, resid, scale):
+    """y (float32, normal, positive) is the round-to-nearest-even of the exact
+    quotient q when |resid| (the exact residual scale * (q - y), fp64) is
+    below scale times half the gap to y's neighbour on q's side, or equal to
+    it with y's last bit even.  The gap is ulp(y) above y, and below y too
+    except at a power of two, where the floats below are twice as dense."""
+    _, e = torch.frexp(y.double())
+    half = scale * torch.ldexp(torch.full_like(resid, 0.5), (e - 24).to(torch.int32))
+    bits = y.view(torch.int32)
+    pow2 = (bits & 0x7FFFFF) == 0
+    lim = torch.where((resid < 0) & pow2, half / 2, half)
+    even = (bits & 1) == 0
+    return (resid.abs() < lim) | ((resid.abs() == lim) & even)
+
+
+def test_div448_correctly_rounded_on_its_range():
+    """The quantizers' group scale without a division: fp32(a / 448) on every
+    fp32 a in [2^-100, 2^128) (448 y is exact in fp64, so a - 448 y is the
+    exact residual)."""
+    lo = int(torch.tensor([2.0 ** -100]).view(torch.int32).item())     # 0x0D800000
+    hi = 0x7F800000                                                       # +inf, excluded
+    say("div448_rn exhaustive on [2^-100, 2^128)")
+    for a in bits_range(lo, hi):
+        y = fl.fp8lin_math_probe(a, 2)
+        ok = _correctly_rounded(y, a.double() - 448.0 * y.double(), 448.0)
+        assert bool(ok.all()), "a = %r: got %r" % (a[~ok][0].item(), y[~ok][0].item())
+
+
+def test_rcp_rn_correctly_rounded_on_its_range():
+    """The quantizers' group reciprocal without a division: fp32(1 / s) on
+    every fp32 s in [2^-92, 2^120) (s y is exact in fp64, so 1 - s y is the
+    exact residual, s times the quotient's)."""
+    lo = int(torch.tensor([2.0 ** -92]).view(torch.int32).item())      # 0x11800000
+    hi = int(torch.tensor([2.0 ** 120]).view(torch.int32).item())      # 0x7B800000
+    say("rcp_rn exhaustive on [2^-92, 2^120)")
+    for s in bits_range(lo, hi):
+        y = fl.fp8lin_math_probe(s, 3)
+        sd = s.double()
+        ok = _correctly_rounded(y, 1.0 - sd * y.double(), sd)
+        assert bool(ok.all()), "s = %r: got %r" % (s[~ok][0].item(), y[~ok][0].item())
