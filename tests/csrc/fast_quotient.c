@@ -2,7 +2,9 @@
  * Host emulation of the GPU quantizers' quotient route, for a CPU test.
  *
  * The kernels compute a group's scale s = fl32(amax / 448) and r = fl32(1 / s)
- * once (IEEE division), then for every element x of the group
+ * once, both correctly rounded (formed on the device without a division and
+ * checked equal to the correctly rounded quotients on every argument by a GPU
+ * test; here by IEEE division), then for every element x of the group
  *     q0 = fl32(x * r);  res = fma(-q0, s, x);  q1 = fma(res, r, q0);
  *     t  = copysign(q1, x)
  * when s >= 2^-92, and t = fl32(x / s) otherwise.  The definition of the code
